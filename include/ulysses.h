@@ -1,0 +1,171 @@
+/*
+ * ulysses.h -- C ABI for one GPU's share of Ulysses sequence parallelism on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Ulysses Sequence Parallelism: Training with Million-Token
+ * Contexts", Hugging Face blog, and "Snowflake's Ulysses trick trains
+ * transformers on million-token contexts across GPUs", second paragraph):
+ * every GPU holds a contiguous block of the sequence; an all-to-all regroups
+ * the data so that each GPU holds the whole sequence for a subset of the
+ * attention heads; each GPU runs ordinary attention on its heads (heads are
+ * independent); a second all-to-all restores the sequence sharding. This
+ * library implements the per-GPU pieces of that path:
+ *
+ *   ulysses_pack     sequence-sharded -> head-sharded layout for one head group
+ *   attn_fwd         causal (optionally packed-document) GQA attention forward
+ *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
+ *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
+ *
+ * Notation: P ranks; T tokens per rank; N = P*T; H heads in a shard tensor;
+ * a head group g owns the hh = H/P contiguous heads [g*hh, (g+1)*hh).
+ * hq / hk = query / key-value heads of the group; G = hq/hk q heads share one
+ * kv head (local q head h reads kv head h / G). D = head dim (64 or 128).
+ *
+ * Layouts (all row-major, D contiguous, no padding):
+ *   shard tensor      [T][H][D]     token-major, one per rank
+ *   head-group tensor [N][hh][D]    what the all-to-all delivers
+ *   lse               float32 [hq][N], natural log of the softmax denominator
+ *   cu_seqlens        int32 [ndocs+1] document offsets into the N tokens
+ *
+ * Element types: ULY_F32 (IEEE float32) or ULY_BF16 (bfloat16 stored as its
+ * 16 raw bits). The attention kernels accumulate in float32; bf16 outputs are
+ * rounded to nearest-even.
+ *
+ * Conventions for every call:
+ *   - The caller owns all memory. The library never allocates, frees or
+ *     synchronises; it only enqueues kernels on `stream` (0 = null stream)
+ *     and returns. A kernel fault surfaces at the caller's next synchronise.
+ *   - All pointers except host_cu and the `shards` arrays themselves are
+ *     device pointers and must be 16-byte aligned. Inputs and outputs must
+ *     not alias.
+ *   - Every argument is checked on the host before any HIP call. A failed
+ *     check returns ULY_ERR_INVALID_ARG (bad value) or ULY_ERR_UNSUPPORTED
+ *     (valid but not implemented), sets the thread-local message returned by
+ *     uly_last_error(), and launches nothing. A failed HIP launch returns
+ *     ULY_ERR_HIP with the HIP error text. Nothing is thrown across the ABI.
+ */
+#ifndef ULYSSES_H_
+#define ULYSSES_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ULY_OK = 0,
+  ULY_ERR_INVALID_ARG = 1,
+  ULY_ERR_UNSUPPORTED = 2,
+  ULY_ERR_HIP = 3
+} uly_status;
+
+typedef enum { ULY_F32 = 0, ULY_BF16 = 1 } uly_dtype;
+
+/* Largest rank count a single pack/unpack call accepts (the shard pointers
+ * travel as kernel arguments). */
+#define ULY_MAX_P 64
+
+/*
+ * ulysses_pack -- the local half of the first all-to-all ("Snowflake's
+ * Ulysses trick ...", second paragraph: afterwards each GPU holds the full
+ * sequence for a subset of heads; "Ulysses Sequence Parallelism ...", the
+ * "Sequence Sharding" step: rank j holds a contiguous block of tokens).
+ *
+ *   out[j*T + t][h][:] = shards[j][t][group*hh + h][:]   j < P, t < T, h < hh
+ *
+ * shards : host array of P device pointers, each to a [T][H][D] tensor (read).
+ * out    : device [P*T][hh][D] (written in full).
+ * P in [1, ULY_MAX_P]; T >= 1; H % P == 0; D in {64, 128}; 0 <= group < P.
+ * The copy is bit-exact (NaN payloads included).
+ */
+uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int D,
+                        uly_dtype dt, int group, void* out, hipStream_t stream);
+
+/*
+ * ulysses_unpack -- the local half of the second all-to-all, which reverses
+ * the first and returns to sequence sharding ("Ulysses Sequence Parallelism
+ * ...", "All-to-All Communication" step).
+ *
+ *   shards[j][t][group*hh + h][:] = in[j*T + t][h][:]
+ *
+ * in     : device [P*T][hh][D] (read).
+ * shards : host array of P device pointers to [T][H][D] tensors; only the
+ *          group's heads are written, every other head is left untouched.
+ * Same preconditions as ulysses_pack; bit-exact.
+ */
+uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt,
+                          int group, void* const* shards, hipStream_t stream);
+
+/*
+ * attn_fwd -- exact softmax attention for one head group over the full
+ * sequence ("Snowflake's Ulysses trick ...", second paragraph: each GPU runs
+ * standard attention on its heads; "Ulysses Sequence Parallelism ...": tiled
+ * attention keeps memory linear while computing the same result).
+ *
+ * For local q head h (kv head h/G), query i and key j, with the mask
+ * M_ij = (j <= i) and doc(j) == doc(i):
+ *   S_ij = softmax_scale * q_i . k_j              (masked: -inf)
+ *   lse_i = log sum_j exp(S_ij)                   (natural log)
+ *   o_i  = sum_j exp(S_ij - lse_i) v_j
+ *
+ * q, o     : device [N][hq][D] of dt.   k, v : device [N][hk][D] of dt.
+ * lse      : device float32 [hq][N] (written; attn_bwd reads it).
+ * cu_seqlens : device int32 [ndocs+1], non-decreasing from 0 to N (empty
+ *            documents allowed), or NULL for one document of N tokens. Its
+ *            contents are a precondition, not checked here (see
+ *            uly_check_cu_seqlens); ndocs is ignored when it is NULL.
+ * N >= 1; hq % hk == 0; D in {64, 128}; softmax_scale finite and > 0;
+ * causal must be 1 (non-causal returns ULY_ERR_UNSUPPORTED).
+ * ULY_F32 requires D == 64 or 128 and runs in float32 throughout.
+ */
+uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t N, int hq, int hk, int D, uly_dtype dt,
+                    const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                    hipStream_t stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
+ * these sizes (currently the per-row delta_i = dO_i . O_i, float32 [hq][N]).
+ */
+uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype dt,
+                                   size_t* bytes);
+
+/*
+ * attn_bwd -- gradients of L = sum(dout * o) for attn_fwd's outputs, with the
+ * softmax probabilities recomputed from lse:
+ *   delta_i = dout_i . o_i
+ *   P_ij  = exp(S_ij - lse_i)            dP_ij = dout_i . v_j
+ *   dS_ij = P_ij (dP_ij - delta_i)
+ *   dq_i  = scale * sum_j dS_ij k_j
+ *   dk_j  = scale * sum_{h in group} sum_i dS_ij q_i
+ *   dv_j  = sum_{h in group} sum_i P_ij dout_i
+ * q, o, dout, dq : device [N][hq][D]; k, v, dk, dv : device [N][hk][D];
+ * lse : device float32 [hq][N] from attn_fwd with the same inputs.
+ * dq, dk, dv are overwritten (dk/dv hold the sum over the G q heads of each
+ * kv head). workspace: device memory of at least attn_bwd_workspace_size()
+ * bytes, 16-byte aligned, owned by the caller, contents ignored.
+ * Other preconditions as attn_fwd.
+ */
+uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    int64_t N, int hq, int hk, int D, uly_dtype dt,
+                    const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * Never NULL; valid until the next call on the same thread. */
+const char* uly_last_error(void);
+
+/* Host-side check of document offsets: host_cu[0] == 0, non-decreasing,
+ * host_cu[ndocs] == N, ndocs >= 1. Returns ULY_OK or ULY_ERR_INVALID_ARG. */
+uly_status uly_check_cu_seqlens(const int32_t* host_cu, int ndocs, int64_t N);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H_ */

@@ -1,0 +1,29 @@
+"""One GPU's share of Ulysses sequence parallelism on MI355X (gfx950).
+
+The hot path -- sequence->head pack, causal GQA/varlen attention forward and
+backward for one head group, head->sequence unpack -- runs in hand-written HIP
+kernels behind the C ABI declared in include/ulysses.h. This package is the
+thin Python binding of that library (same names, argument marshalling only)
+plus its build step.
+"""
+from ._lib import (  # noqa: F401
+    LIB_NAME,
+    SIGNATURES,
+    ULY_BF16,
+    ULY_ERR_HIP,
+    ULY_ERR_INVALID_ARG,
+    ULY_ERR_UNSUPPORTED,
+    ULY_F32,
+    ULY_MAX_P,
+    ULY_OK,
+    UlyssesError,
+    attn_bwd,
+    attn_bwd_workspace_size,
+    attn_fwd,
+    last_error,
+    lib,
+    lib_path,
+    uly_check_cu_seqlens,
+    ulysses_pack,
+    ulysses_unpack,
+)

@@ -1,0 +1,184 @@
+"""ctypes binding of libulysses.so: argument marshalling only.
+
+Every step of the hot path runs in the HIP library; this module turns torch
+tensors into device pointers and sizes, passes the current HIP stream, and
+turns non-OK statuses into exceptions. There is no fallback: if the library
+is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libulysses.so"
+
+ULY_OK, ULY_ERR_INVALID_ARG, ULY_ERR_UNSUPPORTED, ULY_ERR_HIP = 0, 1, 2, 3
+ULY_F32, ULY_BF16 = 0, 1
+ULY_MAX_P = 64
+
+# name -> (restype, argtypes); mirrors include/ulysses.h
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+SIGNATURES = {
+    "ulysses_pack": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "ulysses_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
+    "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32, _f32, _i32, _vp]),
+    "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
+                        _f32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "uly_last_error": (ctypes.c_char_p, []),
+    "uly_check_cu_seqlens": (_i32, [ctypes.POINTER(ctypes.c_int32), _i32, _i64]),
+}
+
+_lib = None
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: the HIP library must be built (python -c "
+                "'import __graft_entry__ as g; g.build()'); there is no fallback path")
+        cdll = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(cdll, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = cdll
+    return _lib
+
+
+def last_error() -> str:
+    return lib().uly_last_error().decode()
+
+
+def _raise(status: int) -> None:
+    if status != ULY_OK:
+        raise UlyssesError(status, last_error())
+
+
+# ----------------------------------------------------------------- marshalling
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return ULY_F32
+    if t.dtype == torch.bfloat16:
+        return ULY_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, shape, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _cu(cu_seqlens, N):
+    import torch
+    if cu_seqlens is None:
+        return None, 0
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 \
+            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor with >= 2 entries")
+    return ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1
+
+
+# ------------------------------------------------------------------ entry points
+def ulysses_pack(shards: Sequence, group: int, out, stream=None) -> None:
+    """out[j*T + t, h] = shards[j][t, group*hh + h] (see include/ulysses.h)."""
+    P = len(shards)
+    T, H, D = shards[0].shape
+    dt = shards[0].dtype
+    ptrs = (ctypes.c_void_p * P)(*[_dev(s, (T, H, D), dt, f"shards[{j}]").value for j, s in enumerate(shards)])
+    if H % P == 0:
+        _dev(out, (P * T, H // P, D), dt, "out")
+    _raise(lib().ulysses_pack(ptrs, P, T, H, D, _dtype_code(shards[0]), group,
+                              ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+
+
+def ulysses_unpack(inp, group: int, shards: Sequence, stream=None) -> None:
+    """shards[j][t, group*hh + h] = inp[j*T + t, h]; other heads untouched."""
+    P = len(shards)
+    T, H, D = shards[0].shape
+    dt = shards[0].dtype
+    ptrs = (ctypes.c_void_p * P)(*[_dev(s, (T, H, D), dt, f"shards[{j}]").value for j, s in enumerate(shards)])
+    if H % P == 0:
+        _dev(inp, (P * T, H // P, D), dt, "inp")
+    _raise(lib().ulysses_unpack(ctypes.c_void_p(inp.data_ptr()), P, T, H, D, _dtype_code(shards[0]), group,
+                                ptrs, _stream(stream)))
+
+
+def attn_fwd(q, k, v, o, lse, softmax_scale: float, cu_seqlens=None, causal: int = 1, stream=None) -> None:
+    """Causal GQA attention forward for one head group (see include/ulysses.h)."""
+    import torch
+    N, hq, D = q.shape
+    hk = k.shape[1]
+    dt = q.dtype
+    args = [_dev(q, (N, hq, D), dt, "q"), _dev(k, (N, hk, D), dt, "k"), _dev(v, (N, hk, D), dt, "v"),
+            _dev(o, (N, hq, D), dt, "o"), _dev(lse, (hq, N), torch.float32, "lse")]
+    cu, nd = _cu(cu_seqlens, N)
+    _raise(lib().attn_fwd(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
+                          _stream(stream)))
+
+
+def attn_bwd_workspace_size(N: int, hq: int, hk: int, D: int, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    code = ULY_BF16 if str(dtype).endswith("bfloat16") else ULY_F32
+    _raise(lib().attn_bwd_workspace_size(N, hq, hk, D, code, ctypes.byref(out)))
+    return out.value
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, cu_seqlens=None,
+             causal: int = 1, stream=None) -> None:
+    """Gradients dq, dk, dv of sum(dout * o) (see include/ulysses.h)."""
+    import torch
+    N, hq, D = q.shape
+    hk = k.shape[1]
+    dt = q.dtype
+    args = [_dev(q, (N, hq, D), dt, "q"), _dev(k, (N, hk, D), dt, "k"), _dev(v, (N, hk, D), dt, "v"),
+            _dev(o, (N, hq, D), dt, "o"), _dev(dout, (N, hq, D), dt, "dout"),
+            _dev(lse, (hq, N), torch.float32, "lse"), _dev(dq, (N, hq, D), dt, "dq"),
+            _dev(dk, (N, hk, D), dt, "dk"), _dev(dv, (N, hk, D), dt, "dv")]
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    cu, nd = _cu(cu_seqlens, N)
+    _raise(lib().attn_bwd(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
+                          ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream)))
+
+
+def uly_check_cu_seqlens(host_cu, N: int) -> None:
+    """Host check of document offsets (a sequence of ints or an int32 array)."""
+    vals = [int(x) for x in host_cu]
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    _raise(lib().uly_check_cu_seqlens(arr, len(vals) - 1, N))

@@ -1,0 +1,173 @@
+// C ABI entry points: host-side argument checks, then one launcher call.
+// Every check runs before any HIP call, so invalid arguments are reported
+// without touching the GPU (and can be tested on a machine without one).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+uly_status fail(uly_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+uly_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ULY_OK;
+  return fail(ULY_ERR_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(uly_dtype dt) { return dt == ULY_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == ULY_F32 || dt == ULY_BF16; }
+
+#define CHECK(cond, status, ...)              \
+  do {                                        \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+uly_status check_permute(const char* fn, int P, int64_t T, int H, int D, int dt, int group,
+                         uly::PermuteDesc* out) {
+  CHECK(P >= 1 && P <= ULY_MAX_P, ULY_ERR_INVALID_ARG, "%s: P=%d must be in [1, %d]", fn, P, ULY_MAX_P);
+  CHECK(T >= 1, ULY_ERR_INVALID_ARG, "%s: T=%lld must be >= 1", fn, (long long)T);
+  CHECK(H >= 1 && H % P == 0, ULY_ERR_INVALID_ARG, "%s: H=%d must be a positive multiple of P=%d", fn, H, P);
+  CHECK(D == 64 || D == 128, ULY_ERR_INVALID_ARG, "%s: D=%d must be 64 or 128", fn, D);
+  CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
+  CHECK(group >= 0 && group < P, ULY_ERR_INVALID_ARG, "%s: group=%d must be in [0, P=%d)", fn, group, P);
+  const int64_t e = elem_bytes(static_cast<uly_dtype>(dt));
+  const int64_t hh = H / P;
+  out->P = P;
+  out->T = T;
+  out->row_bytes = H * D * e;
+  out->seg_bytes = hh * D * e;
+  out->head_offset = group * hh * D * e;
+  CHECK(T * (out->seg_bytes / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
+        "%s: one shard's head group (%lld bytes) exceeds 32 GiB", fn, (long long)(T * out->seg_bytes));
+  return ULY_OK;
+}
+
+uly_status check_attn(const char* fn, int64_t N, int hq, int hk, int D, int dt,
+                      const int32_t* cu, int ndocs, float scale, int causal, uly::AttnDesc* d) {
+  CHECK(N >= 1 && N <= (int64_t(1) << 30), ULY_ERR_INVALID_ARG, "%s: N=%lld must be in [1, 2^30]", fn, (long long)N);
+  CHECK(hq >= 1 && hk >= 1 && hq <= 1024, ULY_ERR_INVALID_ARG, "%s: hq=%d, hk=%d must be positive (hq <= 1024)", fn, hq, hk);
+  CHECK(hq % hk == 0, ULY_ERR_INVALID_ARG, "%s: hq=%d must be a multiple of hk=%d", fn, hq, hk);
+  CHECK(D == 64 || D == 128, ULY_ERR_INVALID_ARG, "%s: D=%d must be 64 or 128", fn, D);
+  CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
+  CHECK(std::isfinite(scale) && scale > 0.f, ULY_ERR_INVALID_ARG, "%s: softmax_scale=%g must be finite and > 0", fn, (double)scale);
+  CHECK(causal == 0 || causal == 1, ULY_ERR_INVALID_ARG, "%s: causal=%d must be 0 or 1", fn, causal);
+  CHECK(causal == 1, ULY_ERR_UNSUPPORTED, "%s: only causal attention is implemented", fn);
+  CHECK(cu == nullptr || ndocs >= 1, ULY_ERR_INVALID_ARG, "%s: ndocs=%d must be >= 1 with cu_seqlens", fn, ndocs);
+  CHECK(cu == nullptr || (reinterpret_cast<uintptr_t>(cu) & 3u) == 0, ULY_ERR_INVALID_ARG,
+        "%s: cu_seqlens must be 4-byte aligned", fn);
+  CHECK(cu == nullptr || ndocs <= (1 << 30), ULY_ERR_INVALID_ARG, "%s: ndocs=%d too large", fn, ndocs);
+  d->N = N;
+  d->hq = hq;
+  d->hk = hk;
+  d->D = D;
+  d->dt = static_cast<uly_dtype>(dt);
+  d->cu = cu;
+  d->ndocs = cu ? ndocs : 1;
+  d->scale = scale;
+  return ULY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uly_last_error(void) { return g_last_error.c_str(); }
+
+uly_status uly_check_cu_seqlens(const int32_t* host_cu, int ndocs, int64_t N) {
+  CHECK(host_cu != nullptr, ULY_ERR_INVALID_ARG, "uly_check_cu_seqlens: host_cu is NULL");
+  CHECK(ndocs >= 1, ULY_ERR_INVALID_ARG, "uly_check_cu_seqlens: ndocs=%d must be >= 1", ndocs);
+  CHECK(host_cu[0] == 0, ULY_ERR_INVALID_ARG, "uly_check_cu_seqlens: cu_seqlens[0]=%d must be 0", host_cu[0]);
+  for (int i = 0; i < ndocs; ++i)
+    CHECK(host_cu[i + 1] >= host_cu[i], ULY_ERR_INVALID_ARG,
+          "uly_check_cu_seqlens: offsets decrease at %d (%d > %d)", i, host_cu[i], host_cu[i + 1]);
+  CHECK(host_cu[ndocs] == N, ULY_ERR_INVALID_ARG, "uly_check_cu_seqlens: cu_seqlens[%d]=%d must equal N=%lld",
+        ndocs, host_cu[ndocs], (long long)N);
+  return ULY_OK;
+}
+
+uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int D, uly_dtype dt,
+                        int group, void* out, hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_permute("ulysses_pack", P, T, H, D, dt, group, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr, ULY_ERR_INVALID_ARG, "ulysses_pack: shards is NULL");
+  CHECK(out != nullptr && aligned16(out), ULY_ERR_INVALID_ARG, "ulysses_pack: out is NULL or not 16-byte aligned");
+  for (int j = 0; j < P; ++j)
+    CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
+          "ulysses_pack: shards[%d] is NULL or not 16-byte aligned", j);
+  return from_hip(uly::launch_pack(shards, out, d, stream), "ulysses_pack");
+}
+
+uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt, int group,
+                          void* const* shards, hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_permute("ulysses_unpack", P, T, H, D, dt, group, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr, ULY_ERR_INVALID_ARG, "ulysses_unpack: shards is NULL");
+  CHECK(in != nullptr && aligned16(in), ULY_ERR_INVALID_ARG, "ulysses_unpack: in is NULL or not 16-byte aligned");
+  for (int j = 0; j < P; ++j)
+    CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
+          "ulysses_unpack: shards[%d] is NULL or not 16-byte aligned", j);
+  return from_hip(uly::launch_unpack(in, shards, d, stream), "ulysses_unpack");
+}
+
+uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N,
+                    int hq, int hk, int D, uly_dtype dt, const int32_t* cu_seqlens, int ndocs,
+                    float softmax_scale, int causal, hipStream_t stream) {
+  uly::AttnDesc d;
+  uly_status s = check_attn("attn_fwd", N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
+  if (s != ULY_OK) return s;
+  const void* ptrs[] = {q, k, v, o, lse};
+  const char* names[] = {"q", "k", "v", "o", "lse"};
+  for (int i = 0; i < 5; ++i)
+    CHECK(ptrs[i] != nullptr && aligned16(ptrs[i]), ULY_ERR_INVALID_ARG,
+          "attn_fwd: %s is NULL or not 16-byte aligned", names[i]);
+  return from_hip(uly::launch_attn_fwd(q, k, v, o, lse, d, stream), "attn_fwd");
+}
+
+uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype dt, size_t* bytes) {
+  uly::AttnDesc d;
+  uly_status s = check_attn("attn_bwd_workspace_size", N, hq, hk, D, dt, nullptr, 1, 1.0f, 1, &d);
+  if (s != ULY_OK) return s;
+  CHECK(bytes != nullptr, ULY_ERR_INVALID_ARG, "attn_bwd_workspace_size: bytes is NULL");
+  *bytes = uly::bwd_workspace_bytes(d);
+  return ULY_OK;
+}
+
+uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
+                    uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  uly::AttnDesc d;
+  uly_status s = check_attn("attn_bwd", N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
+  if (s != ULY_OK) return s;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i)
+    CHECK(ptrs[i] != nullptr && aligned16(ptrs[i]), ULY_ERR_INVALID_ARG,
+          "attn_bwd: %s is NULL or not 16-byte aligned", names[i]);
+  const size_t need = uly::bwd_workspace_bytes(d);
+  CHECK(workspace_bytes >= need, ULY_ERR_INVALID_ARG, "attn_bwd: workspace_bytes=%zu < required %zu",
+        workspace_bytes, need);
+  CHECK(need == 0 || (workspace != nullptr && aligned16(workspace)), ULY_ERR_INVALID_ARG,
+        "attn_bwd: workspace is NULL or not 16-byte aligned");
+  return from_hip(uly::launch_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream), "attn_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,351 @@
+// Causal GQA / packed-document attention forward for one head group.
+//
+// Exact softmax attention computed in key tiles with an online (running-max)
+// softmax, so the N x N score matrix is never stored ("Ulysses Sequence
+// Parallelism: Training with Million-Token Contexts": tiled attention keeps
+// memory linear while the compute stays quadratic; "Snowflake's Ulysses trick
+// ...", second paragraph: each GPU runs standard attention over the full
+// sequence for its heads).
+//
+// Work decomposition (one workgroup = 4 waves):
+//   - the Gw = gcd(G, 4) q heads of one kv head that share K/V are folded
+//     into one workgroup, so each K/V tile read from HBM/L2 serves Gw heads;
+//   - every wave owns RW query rows of one q head (RW = 64 for bf16, 32 for
+//     fp32) and keeps them in registers as the MFMA B operand;
+//   - K/V tiles of 64 keys are double-buffered in LDS; global loads of tile
+//     t+2 are in flight while tile t is consumed, one barrier per tile;
+//   - workgroups are launched heaviest causal row-tile first.
+//
+// Per wave and tile the math runs transposed, S^T = K Q^T, so that each lane
+// owns one query column: the row max and row sum of the softmax are per-lane
+// reductions plus one v_permlane32_swap between the two half-waves. The
+// probabilities are then already laid out as the B operand of O^T += V^T P^T;
+// V^T comes from LDS, where bf16 V tiles are stored transposed (keys
+// contiguous, in the order the P fragments need).
+//
+// Masking (key j, query i): j <= i and j >= doc_start(i). Only the diagonal
+// tile and tiles crossing a document start are masked element-wise; tiles
+// that no row of a wave can see are skipped by that wave.
+#include <cmath>
+#include <numeric>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace uly {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int BN = 64;  // keys per tile
+
+struct FwdParams {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* o;
+  float* lse;
+  const int32_t* cu;
+  int ndocs;
+  int N, hq, hk, G, Gw;
+  int n_qtiles;
+  float scale_log2;
+};
+
+template <class Tr, int D>
+struct FwdCfg {
+  static constexpr int E = Tr::kElem;
+  static constexpr int QB = (sizeof(typename Tr::frag_t) == 16) ? 2 : 1;  // 32-row blocks per wave
+  static constexpr int RW = 32 * QB;
+  static constexpr int KS = D / Tr::kStep;  // MFMA steps over D
+  static constexpr int DB = D / 32;         // 32-wide blocks of D
+  static constexpr int PV = BN / Tr::kStep; // MFMA steps over the keys of a tile
+  static constexpr bool kVt = (E == 2);     // bf16 V stored transposed in LDS
+  static constexpr int K_STRIDE = D * E + 16;
+  static constexpr int V_STRIDE = kVt ? BN * E + 16 : D * E + 16;
+  static constexpr int K_BYTES = BN * K_STRIDE;
+  static constexpr int V_BYTES = kVt ? D * V_STRIDE : BN * V_STRIDE;
+  static constexpr int CPR = D * E / 16;              // 16-byte chunks per row
+  static constexpr int K_CH = BN * CPR / kThreads;    // chunks per thread
+  static constexpr int V_PAIRS = (BN / 4) * (D / 8);  // bf16: (4-key group, 8-dim chunk)
+  static constexpr int V_REGS = kVt ? 4 : K_CH;
+  static_assert(BN * CPR % kThreads == 0, "tile must split evenly");
+  static_assert(!kVt || V_PAIRS <= kThreads, "one V pair per thread at most");
+};
+
+// Position of the 4-key group `sub` (0..3) inside a 16-key group of the
+// transposed V tile: order [keys 0-3, 8-11, 4-7, 12-15], so that half-wave h
+// reads keys {4h..4h+3, 8+4h..8+4h+3} -- the keys its P fragment holds -- as
+// one 16-byte run.
+__device__ __forceinline__ int vt_slot(int kg) {
+  const int sub = kg & 3;
+  return (kg >> 2) * 16 + ((sub & 1) << 3) + ((sub >> 1) << 2);
+}
+
+template <class Tr, int D>
+struct Tile {
+  using C = FwdCfg<Tr, D>;
+  u32x4_t k[C::K_CH];
+  u32x4_t v[C::V_REGS];
+
+  __device__ __forceinline__ void load(const FwdParams& p, int kvh, int kv0, int tid) {
+    const int64_t row_bytes = int64_t(p.hk) * D * C::E;
+    const char* kb = p.k + int64_t(kvh) * D * C::E;
+    const char* vb = p.v + int64_t(kvh) * D * C::E;
+#pragma unroll
+    for (int i = 0; i < C::K_CH; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / C::CPR, col = c % C::CPR;
+      const int key = kv0 + row;
+      k[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(kb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+      if constexpr (!C::kVt)
+        v[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(vb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+    }
+    if constexpr (C::kVt) {
+      if (tid < C::V_PAIRS) {
+        const int kg = tid % (BN / 4), dc = tid / (BN / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kv0 + 4 * kg + i;
+          v[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(vb + key * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(char* lk, char* lv, int tid) const {
+#pragma unroll
+    for (int i = 0; i < C::K_CH; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / C::CPR, col = c % C::CPR;
+      *reinterpret_cast<u32x4_t*>(lk + row * C::K_STRIDE + col * 16) = k[i];
+      if constexpr (!C::kVt) *reinterpret_cast<u32x4_t*>(lv + row * C::V_STRIDE + col * 16) = v[i];
+    }
+    if constexpr (C::kVt) {
+      if (tid < C::V_PAIRS) {
+        // v[i] = key (4kg+i), dims dc*8 .. dc*8+7; word j holds dims 2j (low) and 2j+1 (high).
+        const int kg = tid % (BN / 4), dc = tid / (BN / 4);
+        char* base = lv + vt_slot(kg) * C::E;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = v[0][j], w1 = v[1][j], w2 = v[2][j], w3 = v[3][j];
+          u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+          u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
+          *reinterpret_cast<u32x2_t*>(base + (dc * 8 + 2 * j) * C::V_STRIDE) = lo;
+          *reinterpret_cast<u32x2_t*>(base + (dc * 8 + 2 * j + 1) * C::V_STRIDE) = hi;
+        }
+      }
+    }
+  }
+};
+
+template <class Tr, int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
+  using C = FwdCfg<Tr, D>;
+  using frag_t = typename Tr::frag_t;
+  constexpr int E = C::E, QB = C::QB, RW = C::RW;
+  __shared__ __attribute__((aligned(16))) char smem[2 * (C::K_BYTES + C::V_BYTES)];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int groups = p.G / p.Gw;
+  const int kvh = blockIdx.y / groups, sub = blockIdx.y % groups;
+  const int QW = kWaves / p.Gw;
+  const int qtile = p.n_qtiles - 1 - int(blockIdx.x);  // heaviest first
+  const int wg_q0 = qtile * RW * QW;
+  const int wg_q1 = min(p.N, wg_q0 + RW * QW);
+  const int head = kvh * p.G + sub * p.Gw + (w % p.Gw);
+  const int qbase = wg_q0 + (w / p.Gw) * RW;
+  const bool active = qbase < p.N;
+  const int wq_last = min(qbase + RW - 1, p.N - 1);
+
+  // Query rows of this lane, their document starts, and the wave's bounds.
+  int my_q[QB], my_ds[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    my_q[qb] = qbase + qb * 32 + l32;
+    my_ds[qb] = doc_of(p.cu, p.ndocs, p.N, min(my_q[qb], p.N - 1)).start;
+  }
+  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
+  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+
+  // Q fragments (B operand of S^T = K Q^T), zero past N.
+  frag_t qf[QB][C::KS];
+  const int64_t q_row = int64_t(p.hq) * D * E;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const char* src = p.q + int64_t(my_q[qb]) * q_row + int64_t(head) * D * E + half * Tr::kEpl * E;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qf[qb][ks] = my_q[qb] < p.N ? load_frag<Tr>(src + ks * Tr::kStep * E) : frag_t{};
+  }
+
+  f32x16_t acc_o[C::DB][QB];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc_o[db][qb] = f32x16_t{};
+  }
+
+  const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
+  const int t0 = kv_begin / BN, t1 = (wg_q1 - 1) / BN;
+
+  Tile<Tr, D> tile;
+  tile.load(p, kvh, t0 * BN, tid);
+  tile.store(smem, smem + C::K_BYTES, tid);
+  __syncthreads();
+  if (t0 + 1 <= t1) tile.load(p, kvh, (t0 + 1) * BN, tid);
+
+  for (int t = t0; t <= t1; ++t) {
+    const int kv0 = t * BN;
+    const char* lk = smem + ((t - t0) & 1) * (C::K_BYTES + C::V_BYTES);
+    const char* lv = lk + C::K_BYTES;
+
+    if (active && kv0 <= wq_last && kv0 + BN > w_ds_first) {
+      // S^T tile: keys (2 blocks of 32) x this wave's query columns.
+      f32x16_t s[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const frag_t a = load_frag<Tr>(lk + (kb * 32 + l32) * C::K_STRIDE + (ks * Tr::kStep + half * Tr::kEpl) * E);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma(a, qf[qb][ks], s[kb][qb]);
+        }
+      }
+
+      const bool need_mask = (kv0 + BN - 1 > qbase) || (kv0 < w_ds_last);
+      frag_t pf[QB][C::PV];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kv0 + kb * 32 + acc_row(r, half);
+              if (key > my_q[qb] || key < my_ds[qb]) s[kb][qb][r] = -INFINITY;
+            }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][qb][r]);
+        mt = xhalf_max(mt);
+        const float m_new = fmaxf(m[qb], mt * p.scale_log2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m[qb] - m_use);
+        m[qb] = m_new;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc_o[db][qb] *= alpha;
+        float pv[32];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(s[kb][qb][r], p.scale_log2, -m_use));
+            pv[kb * 16 + r] = e;
+            l[qb] += e;
+          }
+#pragma unroll
+        for (int st = 0; st < C::PV; ++st) pf[qb][st] = make_frag<Tr>(&pv[st * Tr::kEpl]);
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int st = 0; st < C::PV; ++st) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          frag_t a;
+          if constexpr (C::kVt) {
+            a = load_frag<Tr>(lv + (db * 32 + l32) * C::V_STRIDE + (st * 16 + half * 8) * E);
+          } else {
+            const int key = (st >> 4) * 32 + acc_row(st & 15, half);
+            a = load_frag<Tr>(lv + key * C::V_STRIDE + (db * 32 + l32) * E);
+          }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc_o[db][qb] = mfma(a, pf[qb][st], acc_o[db][qb]);
+        }
+      }
+    }
+
+    if (t + 1 <= t1) {
+      char* nk = smem + ((t + 1 - t0) & 1) * (C::K_BYTES + C::V_BYTES);
+      tile.store(nk, nk + C::K_BYTES, tid);
+      if (t + 2 <= t1) tile.load(p, kvh, (t + 2) * BN, tid);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: normalise, write O (rounded to the I/O type) and the natural-log LSE.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lsum = xhalf_sum(l[qb]);
+    const int q = my_q[qb];
+    if (!active || q >= p.N) continue;
+    const float inv = 1.f / lsum;
+    char* dst = p.o + int64_t(q) * q_row + int64_t(head) * D * E;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + 8 * r4 + 4 * half;
+        const float x0 = acc_o[db][qb][4 * r4 + 0] * inv, x1 = acc_o[db][qb][4 * r4 + 1] * inv;
+        const float x2 = acc_o[db][qb][4 * r4 + 2] * inv, x3 = acc_o[db][qb][4 * r4 + 3] * inv;
+        if constexpr (E == 2) {
+          *reinterpret_cast<u32x2_t*>(dst + d * E) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        } else {
+          *reinterpret_cast<u32x4_t*>(dst + d * E) =
+              u32x4_t{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)};
+        }
+      }
+    if (half == 0) p.lse[int64_t(head) * p.N + q] = (m[qb] + log2f(lsum)) * kLn2;
+  }
+}
+
+template <class Tr, int D>
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, const AttnDesc& d,
+                  hipStream_t stream) {
+  using C = FwdCfg<Tr, D>;
+  FwdParams p;
+  p.q = static_cast<const char*>(q);
+  p.k = static_cast<const char*>(k);
+  p.v = static_cast<const char*>(v);
+  p.o = static_cast<char*>(o);
+  p.lse = lse;
+  p.cu = d.cu;
+  p.ndocs = d.ndocs;
+  p.N = static_cast<int>(d.N);
+  p.hq = d.hq;
+  p.hk = d.hk;
+  p.G = d.hq / d.hk;
+  p.Gw = std::gcd(p.G, kWaves);
+  const int rows = C::RW * (kWaves / p.Gw);
+  p.n_qtiles = static_cast<int>((d.N + rows - 1) / rows);
+  p.scale_log2 = d.scale * kLog2e;
+  dim3 grid(p.n_qtiles, d.hk * (p.G / p.Gw));
+  attn_fwd_kernel<Tr, D><<<grid, kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const AttnDesc& d, hipStream_t stream) {
+  if (d.dt == ULY_BF16)
+    return d.D == 128 ? launch<TrBF16, 128>(q, k, v, o, lse, d, stream)
+                      : launch<TrBF16, 64>(q, k, v, o, lse, d, stream);
+  return d.D == 128 ? launch<TrF32, 128>(q, k, v, o, lse, d, stream)
+                    : launch<TrF32, 64>(q, k, v, o, lse, d, stream);
+}
+
+}  // namespace uly

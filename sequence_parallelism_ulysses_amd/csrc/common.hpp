@@ -1,0 +1,109 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ulysses.h"
+
+namespace uly {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 32x32 output tile of a v_mfma_f32_32x32x* instruction, as held by lane l,
+// accumulator slot r (checked on gfx950):
+//   column = l % 32,  row = 8*(r/4) + 4*(l/32) + (r%4).
+// Operand A (rows x k) is read by lane l as row l%32; operand B (k x cols) as
+// column l%32; the k values a lane supplies are paired between A and B by
+// lane half (l/32) and position within the lane.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Combine a per-lane value with the same lane of the other half-wave
+// (lane l and lane l^32): v_permlane32_swap hands each lane both values.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(to_bf16_bits(lo)) | (uint32_t(to_bf16_bits(hi)) << 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Document containing token t: offsets cu[0..ndocs] are non-decreasing from
+// 0 to N, and t < N. Returns its [start, end). cu == nullptr: one document.
+struct DocSpan {
+  int start, end;
+};
+__device__ __forceinline__ DocSpan doc_of(const int32_t* __restrict__ cu, int ndocs, int N, int t) {
+  if (cu == nullptr) return {0, N};
+  int lo = 0, hi = ndocs;  // cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  return {cu[lo], cu[hi]};
+}
+
+// Element traits: bf16 uses v_mfma_f32_32x32x16_bf16 (8 k-values per lane),
+// fp32 uses v_mfma_f32_32x32x2f32 (1 k-value per lane).
+struct TrBF16 {
+  using frag_t = bf16x8_t;
+  static constexpr int kElem = 2;
+  static constexpr int kStep = 16;  // k per instruction
+  static constexpr int kEpl = 8;    // k values per lane
+  static constexpr uly_dtype kDtype = ULY_BF16;
+};
+struct TrF32 {
+  using frag_t = float;
+  static constexpr int kElem = 4;
+  static constexpr int kStep = 2;
+  static constexpr int kEpl = 1;
+  static constexpr uly_dtype kDtype = ULY_F32;
+};
+
+// Load one operand fragment (kEpl contiguous elements) from a byte address.
+template <class Tr>
+__device__ __forceinline__ typename Tr::frag_t load_frag(const void* p) {
+  return *reinterpret_cast<const typename Tr::frag_t*>(p);
+}
+
+// Build a fragment from kEpl fp32 values (rounded to bf16 for TrBF16).
+template <class Tr>
+__device__ __forceinline__ typename Tr::frag_t make_frag(const float* v);
+template <>
+__device__ __forceinline__ bf16x8_t make_frag<TrBF16>(const float* v) {
+  u32x4_t w;
+  w[0] = pack_bf16x2(v[0], v[1]);
+  w[1] = pack_bf16x2(v[2], v[3]);
+  w[2] = pack_bf16x2(v[4], v[5]);
+  w[3] = pack_bf16x2(v[6], v[7]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+template <>
+__device__ __forceinline__ float make_frag<TrF32>(const float* v) { return v[0]; }
+
+}  // namespace uly

@@ -1,0 +1,44 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by api.cpp and only
+// enqueues work on `stream`; it returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ulysses.h"
+
+namespace uly {
+
+// Byte-level description of one pack/unpack call.
+struct PermuteDesc {
+  int P;
+  int64_t T;             // tokens per shard
+  int64_t row_bytes;     // H * D * elem   (one token of a shard)
+  int64_t seg_bytes;     // hh * D * elem  (one token of the head group)
+  int64_t head_offset;   // group * hh * D * elem
+};
+
+hipError_t launch_pack(const void* const* shards, void* out, const PermuteDesc& d,
+                       hipStream_t stream);
+hipError_t launch_unpack(const void* in, void* const* shards, const PermuteDesc& d,
+                         hipStream_t stream);
+
+struct AttnDesc {
+  int64_t N;
+  int hq, hk, D;
+  uly_dtype dt;
+  const int32_t* cu;     // device, or nullptr
+  int ndocs;             // number of documents (1 when cu is nullptr)
+  float scale;
+};
+
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const AttnDesc& d, hipStream_t stream);
+
+size_t bwd_workspace_bytes(const AttnDesc& d);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* workspace, const AttnDesc& d, hipStream_t stream);
+
+}  // namespace uly

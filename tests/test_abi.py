@@ -1,0 +1,177 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/ulysses.h declares, and rejects bad arguments on the host with a
+status code and a message before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sequence_parallelism_ulysses_amd as uly
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(uly.lib_path()), reason="libulysses.so not built")
+
+# A fake, 16-byte-aligned device address. Only invalid-argument paths are
+# exercised, which return before anything dereferences or launches.
+FAKE = 0x7F0000001000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "uly_check_cu_seqlens", "uly_last_error",
+        "ulysses_pack", "ulysses_unpack"])
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(uly.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(uly.SIGNATURES)
+
+
+def _ptrs(n, base=FAKE):
+    return (ctypes.c_void_p * n)(*[base + 4096 * i for i in range(n)])
+
+
+def _pack(**kw):
+    a = dict(shards=_ptrs(4), P=4, T=256, H=8, D=64, dt=uly.ULY_F32, group=0, out=FAKE, stream=None)
+    a.update(kw)
+    return uly.lib().ulysses_pack(a["shards"], a["P"], a["T"], a["H"], a["D"], a["dt"], a["group"], a["out"], a["stream"])
+
+
+def _unpack(**kw):
+    a = dict(inp=FAKE, P=4, T=256, H=8, D=64, dt=uly.ULY_BF16, group=0, shards=_ptrs(4), stream=None)
+    a.update(kw)
+    return uly.lib().ulysses_unpack(a["inp"], a["P"], a["T"], a["H"], a["D"], a["dt"], a["group"], a["shards"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(P=0, shards=_ptrs(1)), uly.ULY_ERR_INVALID_ARG, "P=0"),
+    (dict(P=65, shards=_ptrs(65)), uly.ULY_ERR_INVALID_ARG, "P=65"),
+    (dict(T=0), uly.ULY_ERR_INVALID_ARG, "T=0"),
+    (dict(H=6), uly.ULY_ERR_INVALID_ARG, "H=6"),
+    (dict(D=96), uly.ULY_ERR_INVALID_ARG, "D=96"),
+    (dict(dt=7), uly.ULY_ERR_INVALID_ARG, "dtype"),
+    (dict(group=4), uly.ULY_ERR_INVALID_ARG, "group=4"),
+    (dict(group=-1), uly.ULY_ERR_INVALID_ARG, "group=-1"),
+    (dict(out=None), uly.ULY_ERR_INVALID_ARG, "out"),
+    (dict(out=FAKE + 8), uly.ULY_ERR_INVALID_ARG, "aligned"),
+    (dict(shards=(ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)), uly.ULY_ERR_INVALID_ARG, "shards[2]"),
+    (dict(shards=(ctypes.c_void_p * 4)(FAKE, FAKE + 4, FAKE, FAKE)), uly.ULY_ERR_INVALID_ARG, "shards[1]"),
+    (dict(T=1 << 26, H=64, D=128, P=1, shards=_ptrs(1)), uly.ULY_ERR_UNSUPPORTED, "32 GiB"),
+])
+def test_pack_rejects(kw, status, needle):
+    assert _pack(**kw) == status
+    assert needle in uly.last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(inp=None), "in is NULL"), (dict(H=9), "H=9"), (dict(group=5), "group=5"),
+    (dict(shards=(ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, None)), "shards[3]"),
+])
+def test_unpack_rejects(kw, needle):
+    assert _unpack(**kw) == uly.ULY_ERR_INVALID_ARG
+    assert needle in uly.last_error()
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, N=1024, hq=4, hk=1, D=128, dt=uly.ULY_BF16,
+             cu=None, nd=0, scale=0.088, causal=1, stream=None)
+    a.update(kw)
+    return uly.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["N"], a["hq"], a["hk"], a["D"], a["dt"],
+                              a["cu"], a["nd"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(N=0), uly.ULY_ERR_INVALID_ARG, "N=0"),
+    (dict(hq=3, hk=2), uly.ULY_ERR_INVALID_ARG, "multiple"),
+    (dict(hk=0), uly.ULY_ERR_INVALID_ARG, "hk=0"),
+    (dict(D=32), uly.ULY_ERR_INVALID_ARG, "D=32"),
+    (dict(dt=2), uly.ULY_ERR_INVALID_ARG, "dtype"),
+    (dict(scale=0.0), uly.ULY_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(scale=float("nan")), uly.ULY_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(scale=float("inf")), uly.ULY_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(causal=0), uly.ULY_ERR_UNSUPPORTED, "causal"),
+    (dict(causal=2), uly.ULY_ERR_INVALID_ARG, "causal=2"),
+    (dict(cu=FAKE, nd=0), uly.ULY_ERR_INVALID_ARG, "ndocs=0"),
+    (dict(cu=FAKE + 2, nd=3), uly.ULY_ERR_INVALID_ARG, "4-byte"),
+    (dict(q=None), uly.ULY_ERR_INVALID_ARG, "q is NULL"),
+    (dict(lse=FAKE + 4), uly.ULY_ERR_INVALID_ARG, "lse"),
+    (dict(v=FAKE + 1), uly.ULY_ERR_INVALID_ARG, "v is NULL or not"),
+])
+def test_attn_fwd_rejects(kw, status, needle):
+    assert _fwd(**kw) == status
+    assert needle in uly.last_error()
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, N=1024, hq=4, hk=1,
+             D=128, dt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return uly.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["N"],
+                              a["hq"], a["hk"], a["D"], a["dt"], a["cu"], a["nd"], a["scale"], a["causal"], a["ws"],
+                              a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dk=None), uly.ULY_ERR_INVALID_ARG, "dk is NULL"),
+    (dict(do=FAKE + 2), uly.ULY_ERR_INVALID_ARG, "dout"),
+    (dict(wsb=16), uly.ULY_ERR_INVALID_ARG, "workspace_bytes"),
+    (dict(ws=None), uly.ULY_ERR_INVALID_ARG, "workspace"),
+    (dict(causal=0), uly.ULY_ERR_UNSUPPORTED, "causal"),
+    (dict(D=256), uly.ULY_ERR_INVALID_ARG, "D=256"),
+    (dict(N=-5), uly.ULY_ERR_INVALID_ARG, "N=-5"),
+])
+def test_attn_bwd_rejects(kw, status, needle):
+    assert _bwd(**kw) == status
+    assert needle in uly.last_error()
+
+
+def test_workspace_size():
+    n = ctypes.c_size_t(0)
+    assert uly.lib().attn_bwd_workspace_size(32768, 4, 1, 128, uly.ULY_BF16, ctypes.byref(n)) == uly.ULY_OK
+    assert n.value >= 4 * 4 * 32768
+    assert uly.lib().attn_bwd_workspace_size(32768, 4, 3, 128, uly.ULY_BF16, ctypes.byref(n)) == uly.ULY_ERR_INVALID_ARG
+    assert uly.lib().attn_bwd_workspace_size(32768, 4, 1, 128, uly.ULY_BF16, None) == uly.ULY_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cu,N,ok", [
+    ([0, 5], 5, True), ([0, 3, 3, 5], 5, True), ([0, 0, 5, 5], 5, True),
+    ([1, 5], 5, False), ([0, 4, 3, 5], 5, False), ([0, 3], 5, False), ([0], 0, False),
+])
+def test_check_cu_seqlens(cu, N, ok):
+    if ok:
+        uly.uly_check_cu_seqlens(cu, N)
+        assert uly.lib().uly_check_cu_seqlens((ctypes.c_int32 * len(cu))(*cu), len(cu) - 1, N) == uly.ULY_OK
+    else:
+        with pytest.raises(uly.UlyssesError) as e:
+            uly.uly_check_cu_seqlens(cu, N)
+        assert e.value.status == uly.ULY_ERR_INVALID_ARG and "uly_check_cu_seqlens" in e.value.message
+
+
+def test_null_cu_pointer_rejected():
+    assert uly.lib().uly_check_cu_seqlens(None, 1, 5) == uly.ULY_ERR_INVALID_ARG
+
+
+def test_last_error_is_thread_local():
+    import threading
+    _fwd(N=0)
+    msgs = {}
+
+    def other():
+        msgs["t"] = uly.last_error()
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert msgs["t"] == ""
+    assert "N=0" in uly.last_error()

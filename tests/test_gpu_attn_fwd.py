@@ -1,0 +1,78 @@
+"""GPU parity of attn_fwd (reached through ulysses_pack from seeded shards)
+against the fp64 oracle.
+
+Tolerances: fp32 workload max-abs <= 1e-4 (O and LSE); bf16 O within
+max(2e-2, one bf16 ulp of |ref|) element-wise, LSE (fp32 output) within 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sequence_parallelism_ulysses_amd as uly
+import synthetic as syn
+from harness import DEV, Run, assert_close, bf16_tol, dev_to_bits, decode, oracle_attention, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(run):
+    c = run.cfg
+    q, k, v = run.packed("q"), run.packed("k"), run.packed("v")
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((c.hq, c.N), float("nan"), dtype=torch.float32, device=DEV)
+    uly.attn_fwd(q, k, v, o, lse, c.scale, run.cu_dev)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_fwd(run, rows=None):
+    c = run.cfg
+    o, lse = run_fwd(run)
+    ref = oracle_attention(run, rows=rows, backward=False)
+    sel = slice(None) if rows is None else torch.from_numpy(rows).to(DEV)
+    got_o = decode(dev_to_bits(o[sel]))
+    got_lse = lse[:, sel].cpu().numpy().astype(np.float64)
+    if c.dtype == "f32":
+        assert_close(got_o, ref["o"], 1e-4, "O")
+        assert_close(got_lse, ref["lse"], 1e-4, "LSE")
+    else:
+        assert_close(got_o, ref["o"], bf16_tol(ref["o"]), "O")
+        assert_close(got_lse, ref["lse"], 1e-3, "LSE")
+    return o, lse
+
+
+def test_fwd_c1_fp32_full():
+    check_fwd(Run(syn.CONFIGS["c1"], tensors=("q", "k", "v")))
+
+
+SMALL = [
+    # N, P, Hq, Hkv, D, dtype, doc lengths (None = one document)
+    (1000, 8, 32, 8, 128, "bf16", None),                       # ragged N, GQA 4:1
+    (3000, 8, 32, 8, 128, "bf16", [1, 700, 0, 129, 1000, 1170]),  # packed docs, empty and 1-token docs
+    (777, 7, 14, 14, 64, "bf16", None),                        # D=64, no GQA (2 heads, 2 kv heads)
+    (512, 4, 32, 8, 128, "bf16", [64, 64, 128, 256]),          # 8 q heads over 2 kv heads, tile-aligned docs
+    (300, 2, 12, 4, 128, "bf16", [150, 150]),                  # G=3: one q head per workgroup
+    (333, 3, 6, 3, 128, "f32", None),                          # fp32 D=128, GQA 2:1
+    (64, 1, 4, 1, 64, "f32", [10, 54]),                        # one tile, fp32 D=64
+    (8, 8, 8, 8, 128, "bf16", None),                           # fewer tokens than a tile
+]
+
+
+@pytest.mark.parametrize("N,P,Hq,Hkv,D,dtype,lens", SMALL)
+def test_fwd_small_full(N, P, Hq, Hkv, D, dtype, lens):
+    cfg = syn.custom(N, P, Hq, Hkv, D, dtype, seed=N + D)
+    cu = None if lens is None else syn.cu_from_lengths(lens)
+    check_fwd(Run(cfg, cu=cu, tensors=("q", "k", "v")))
+
+
+@pytest.mark.parametrize("key", ["c2", "c5"])
+def test_fwd_workload_sampled_rows(key):
+    cfg = syn.CONFIGS[key]
+    run = Run(cfg, tensors=("q", "k", "v"))
+    check_fwd(run, rows=sample_rows(cfg.N, run.cu_host))
+
+
+def test_fwd_c3_sampled_rows():
+    cfg = syn.CONFIGS["c3"]
+    run = Run(cfg, tensors=("q", "k", "v"))
+    check_fwd(run, rows=sample_rows(cfg.N, None, n_random=64))

@@ -1,0 +1,118 @@
+"""GPU parity of ulysses_pack / ulysses_unpack: bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import sequence_parallelism_ulysses_amd as uly
+import synthetic as syn
+from oracle import pack_ref, unpack_ref
+from harness import DEV, bits_to_dev, dev_to_bits
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (P, T, H, D, dtype)
+    (4, 256, 8, 64, "f32"),      # c1 shards
+    (8, 4096, 32, 128, "bf16"),  # c2 q/do shards
+    (8, 4096, 8, 128, "bf16"),   # c2 k/v shards
+    (3, 7, 6, 64, "bf16"),       # ragged: odd T, 2 heads per group
+    (1, 5, 3, 128, "f32"),       # one rank: pack is a copy of the whole shard
+    (5, 33, 15, 128, "bf16"),    # 3 heads per group
+    (64, 2, 64, 64, "bf16"),     # the largest rank count
+]
+
+
+def _host_shards(P, T, H, D, dtype, seed):
+    r = np.random.default_rng(seed)
+    dt = np.uint16 if dtype == "bf16" else np.uint32
+    return [r.integers(0, np.iinfo(dt).max, size=(T, H, D), dtype=dt, endpoint=True) for _ in range(P)]
+
+
+@pytest.mark.parametrize("P,T,H,D,dtype", CASES)
+def test_pack_unpack_bit_exact(P, T, H, D, dtype):
+    # raw random bits (NaN payloads and denormals included) must survive
+    host = _host_shards(P, T, H, D, dtype, seed=P * 1000 + T)
+    dev = [bits_to_dev(s) for s in host]
+    hh = H // P
+    groups = sorted({0, P - 1, P // 2})
+    for g in groups:
+        out = torch.empty((P * T, hh, D), dtype=dev[0].dtype, device=DEV)
+        uly.ulysses_pack(dev, g, out)
+        torch.cuda.synchronize()
+        want = pack_ref(host, g)
+        assert np.array_equal(dev_to_bits(out), want), f"pack group {g}"
+        # unpack into canary-filled shards: group heads restored, others untouched
+        canary_bits = np.full((T, H, D), 0x7FA5 if dtype == "bf16" else 0x7FC0A5A5,
+                              dtype=host[0].dtype)
+        canary = [bits_to_dev(canary_bits.copy()) for _ in range(P)]
+        uly.ulysses_unpack(out, g, canary)
+        torch.cuda.synchronize()
+        want_sh = unpack_ref(want, [canary_bits] * P, g)
+        for j in range(P):
+            assert np.array_equal(dev_to_bits(canary[j]), want_sh[j]), f"unpack group {g} shard {j}"
+
+
+def test_pack_all_groups_roundtrip_c2():
+    """Pack every group, unpack every group into zeros: the shards come back."""
+    cfg = syn.CONFIGS["c2"]
+    host = syn.all_shards_bits(cfg, "k")
+    dev = [bits_to_dev(s) for s in host]
+    back = [torch.zeros_like(s) for s in dev]
+    for g in range(cfg.P):
+        out = torch.empty((cfg.N, cfg.hk, cfg.D), dtype=torch.bfloat16, device=DEV)
+        uly.ulysses_pack(dev, g, out)
+        uly.ulysses_unpack(out, g, back)
+    torch.cuda.synchronize()
+    for a, b in zip(back, host):
+        assert np.array_equal(dev_to_bits(a), b)
+
+
+def test_pack_on_side_stream():
+    """The call enqueues on the stream it is given."""
+    host = _host_shards(4, 64, 8, 128, "bf16", seed=3)
+    dev = [bits_to_dev(s) for s in host]
+    out = torch.empty((256, 2, 128), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        uly.ulysses_pack(dev, 1, out)
+    s.synchronize()
+    assert np.array_equal(dev_to_bits(out), pack_ref(host, 1))
+
+
+def test_pack_c4_q_shape_64bit_offsets():
+    """Million-token case: the all-shards Q holds 2^32 elements, so offsets need
+    64 bits. Check the last group on sampled tokens of every shard (including
+    each shard's last token) against the oracle on those rows."""
+    P, T, H, D = 8, 131072, 32, 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(20260313)
+    dev = [torch.randint(-32768, 32767, (T, H, D), dtype=torch.int16, device=DEV, generator=gen).view(torch.bfloat16)
+           for _ in range(P)]
+    g = P - 1
+    out = torch.empty((P * T, H // P, D), dtype=torch.bfloat16, device=DEV)
+    uly.ulysses_pack(dev, g, out)
+    torch.cuda.synchronize()
+    ts = np.array([0, 1, 4095, 65536, T - 2, T - 1])
+    mini = [dev_to_bits(s[torch.from_numpy(ts).to(DEV)]) for s in dev]   # [len(ts), H, D] per shard
+    want = pack_ref(mini, g)                                             # rows j*len(ts) + i
+    rows = np.concatenate([j * T + ts for j in range(P)])
+    got = dev_to_bits(out[torch.from_numpy(rows).to(DEV)])
+    assert np.array_equal(got, want)
+    # and the inverse on the same buffers: write the group back into zeroed heads
+    for s in dev:
+        s.view(torch.int16)[:, g * 4:(g + 1) * 4, :] = 0
+    uly.ulysses_unpack(out, g, dev)
+    torch.cuda.synchronize()
+    for j in range(P):
+        assert np.array_equal(dev_to_bits(dev[j][torch.from_numpy(ts).to(DEV)]), mini[j])
+    del dev, out
+    torch.cuda.empty_cache()
+
+
+def test_pack_rejects_mismatched_tensors():
+    dev = [torch.zeros((8, 8, 64), dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    with pytest.raises(ValueError):
+        uly.ulysses_pack(dev, 0, torch.zeros((32, 3, 64), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(uly.UlyssesError):
+        uly.ulysses_pack(dev, 4, torch.zeros((32, 2, 64), dtype=torch.bfloat16, device=DEV))
