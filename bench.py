@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of Ulysses sequence parallelism on MI355X.
+
+One step = the whole hot path over one batch of synthetic input, with every
+input already resident in HBM:
+  pack Q, K, V, dO (sequence-sharded -> head group)   4 x ulysses_pack
+  causal attention forward                             attn_fwd
+  causal attention backward                            attn_bwd
+  unpack O, dQ, dK, dV (head group -> sequence-sharded) 4 x ulysses_unpack
+
+Metric: algorithmic causal-attention fwd+bwd TFLOP/s of the step
+(14 * D * C * hq FLOP, C = number of causal (query, key) pairs), with the
+roofline of the dominant call and the oracle timed on the host as a baseline.
+Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def causal_pairs(N: int, cu) -> int:
+    if cu is None:
+        return N * (N + 1) // 2
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    return int((lens * (lens + 1) // 2).sum())
+
+
+def oracle_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
+    """The oracle as it stands, on a bounded sample of the same workload: fp64
+    forward+backward for the last R query rows of the head group (every
+    visible key), R sized to take about `budget_s` seconds."""
+    from oracle import attn_ref, bf16_bits_to_f64, f32_bits_to_f64, pack_ref
+
+    dec = bf16_bits_to_f64 if cfg.dtype == "bf16" else f32_bits_to_f64
+    x = {n: dec(pack_ref(host[n], cfg.group)) for n in ("q", "k", "v", "do")}
+    workers = oracle_threads()
+    _, start = _doc_starts(cfg.N, cu)
+
+    def run(R):
+        rows = np.arange(cfg.N - R, cfg.N)
+        t = time.perf_counter()
+        attn_ref(x["q"], x["k"], x["v"], cfg.scale, cu, do=x["do"], rows=rows, workers=workers)
+        dt = time.perf_counter() - t
+        pairs = int((rows - start[rows] + 1).sum())
+        return dt, pairs
+
+    R = min(cfg.N, 64)
+    dt, pairs = run(R)
+    while dt < budget_s / 4 and R < cfg.N:
+        R = min(cfg.N, int(R * max(2.0, min(8.0, budget_s / max(dt, 1e-3) / 2))))
+        dt, pairs = run(R)
+    flops = 14 * cfg.D * cfg.hq * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"fp64 numpy oracle, forward+backward of the last {R} query rows x {cfg.hq} q heads "
+                      f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}"}
+
+
+def _doc_starts(N, cu):
+    cuv = np.array([0, N]) if cu is None else np.asarray(cu, dtype=np.int64)
+    tok = np.arange(N)
+    doc = np.searchsorted(cuv, tok, side="right") - 1
+    return doc, cuv[doc]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2", help="workload key: c2 (default), c3, c4, c5")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the path on a single GPU; "
+              f"--gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import sequence_parallelism_ulysses_amd as uly
+    import synthetic as syn
+
+    cfg = syn.CONFIGS[args.config]
+    if cfg.dtype != "bf16":
+        print("bench.py times the bf16 workloads (c2..c5)", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    tdt = torch.bfloat16
+    cu = syn.cu_seqlens(cfg)
+    cu_dev = None if cu is None else torch.from_numpy(cu).to(dev)
+
+    host = {n: syn.all_shards_bits(cfg, n) for n in ("q", "k", "v", "do")}
+    shards = {n: [torch.from_numpy(s.view(np.int16)).to(dev).view(tdt) for s in host[n]] for n in host}
+    N, hq, hk, D, P, T, g = cfg.N, cfg.hq, cfg.hk, cfg.D, cfg.P, cfg.T, cfg.group
+    qg = torch.empty((N, hq, D), dtype=tdt, device=dev)
+    kg = torch.empty((N, hk, D), dtype=tdt, device=dev)
+    vg = torch.empty_like(kg)
+    dog = torch.empty_like(qg)
+    o = torch.empty_like(qg)
+    lse = torch.empty((hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    ws = torch.empty(uly.attn_bwd_workspace_size(N, hq, hk, D, tdt), dtype=torch.uint8, device=dev)
+    out_sh = {n: [torch.zeros((T, cfg.heads(n), D), dtype=tdt, device=dev) for _ in range(P)]
+              for n in ("o", "dq", "dk", "dv")}
+
+    calls = [
+        ("pack_q", lambda: uly.ulysses_pack(shards["q"], g, qg)),
+        ("pack_k", lambda: uly.ulysses_pack(shards["k"], g, kg)),
+        ("pack_v", lambda: uly.ulysses_pack(shards["v"], g, vg)),
+        ("pack_do", lambda: uly.ulysses_pack(shards["do"], g, dog)),
+        ("attn_fwd", lambda: uly.attn_fwd(qg, kg, vg, o, lse, cfg.scale, cu_dev)),
+        ("attn_bwd", lambda: uly.attn_bwd(qg, kg, vg, o, dog, lse, dq, dk, dv, cfg.scale, ws, cu_dev)),
+        ("unpack_o", lambda: uly.ulysses_unpack(o, g, out_sh["o"])),
+        ("unpack_dq", lambda: uly.ulysses_unpack(dq, g, out_sh["dq"])),
+        ("unpack_dk", lambda: uly.ulysses_unpack(dk, g, out_sh["dk"])),
+        ("unpack_dv", lambda: uly.ulysses_unpack(dv, g, out_sh["dv"])),
+    ]
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(calls):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # HIP events on the stream the library launches on (torch's current stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    call_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+               for i, (name, _) in enumerate(calls)}
+
+    C = causal_pairs(N, cu)
+    fwd_flop = 4 * D * C * hq
+    bwd_flop = 10 * D * C * hq
+    step_flop = fwd_flop + bwd_flop
+    value = step_flop / (ms_step * 1e-3) / 1e12
+
+    def pack_bytes(name):
+        heads = hq if name.endswith(("_q", "_do", "_o", "_dq")) else hk
+        return 2 * N * heads * D * 2
+    details = {}
+    for name, ms in call_ms.items():
+        if name == "attn_fwd":
+            a = fwd_flop / (ms * 1e-3) / 1e12
+            details[name] = {"ms": round(ms, 4), "TFLOP/s": round(a, 2), "frac_mfma": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+        elif name == "attn_bwd":
+            a = bwd_flop / (ms * 1e-3) / 1e12
+            details[name] = {"ms": round(ms, 4), "TFLOP/s": round(a, 2), "frac_mfma": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            a = pack_bytes(name) / (ms * 1e-3) / 1e9
+            details[name] = {"ms": round(ms, 4), "GB/s": round(a, 1), "frac_hbm": round(a / HBM_PEAK_GBS, 4)}
+
+    dom = max(("attn_fwd", "attn_bwd"), key=lambda n: call_ms[n])
+    dom_flop = bwd_flop if dom == "attn_bwd" else fwd_flop
+    achieved = dom_flop / (call_ms[dom] * 1e-3) / 1e12
+    roofline = {
+        "kernel": dom + (" (delta + dkdv + dq launches)" if dom == "attn_bwd" else ""),
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+        "per_launch": f"{'10' if dom == 'attn_bwd' else '4'}*D*C*hq = {dom_flop:.4g} FLOP, "
+                      f"C = {C} causal pairs, hq = {hq}, D = {D}",
+        "avg_launch_ms": round(call_ms[dom], 4),
+    }
+    pack_total_ms = sum(v for k, v in call_ms.items() if "pack" in k)
+    pack_total_bytes = sum(pack_bytes(k) for k in call_ms if "pack" in k)
+
+    line = {
+        "metric": "causal attn fwd+bwd TFLOP/s per GPU head group (% MFMA peak); pack GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.workload, "N": N, "P": P, "tokens_per_shard": T, "q_heads": hq, "kv_heads": hk,
+                   "head_dim": D, "causal": True, "documents": None if cu is None else int(len(cu) - 1),
+                   "causal_pairs": C, "step_flop": step_flop},
+        "frac_mfma_step": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "pack_unpack": {"GB/s": round(pack_total_bytes / (pack_total_ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(pack_total_bytes / (pack_total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "bytes": pack_total_bytes, "ms": round(pack_total_ms, 4)},
+        "roofline": roofline,
+        "calls": details,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, cu, host, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

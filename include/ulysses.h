@@ -143,16 +143,20 @@ uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype d
  *   dq_i  = scale * sum_j dS_ij k_j
  *   dk_j  = scale * sum_{h in group} sum_i dS_ij q_i
  *   dv_j  = sum_{h in group} sum_i P_ij dout_i
- * q, o, dout, dq : device [N][hq][D]; k, v, dk, dv : device [N][hk][D];
+ * q, o, dout : device [N][hq][D] of dt; k, v : device [N][hk][D] of dt;
  * lse : device float32 [hq][N] from attn_fwd with the same inputs.
+ * dq : device [N][hq][D], dk, dv : device [N][hk][D], all of grad_dt, which
+ * is dt or ULY_F32 (fp32 gradients from bf16 inputs: the same computation,
+ * stored before the final rounding; with grad_dt == dt == ULY_BF16 each
+ * gradient is that fp32 value rounded to nearest even).
  * dq, dk, dv are overwritten (dk/dv hold the sum over the G q heads of each
  * kv head). workspace: device memory of at least attn_bwd_workspace_size()
  * bytes, 16-byte aligned, owned by the caller, contents ignored.
- * Other preconditions as attn_fwd.
+ * Other preconditions as attn_fwd. Results are deterministic (no atomics).
  */
 uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                    int64_t N, int hq, int hk, int D, uly_dtype dt,
+                    int64_t N, int hq, int hk, int D, uly_dtype dt, uly_dtype grad_dt,
                     const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 

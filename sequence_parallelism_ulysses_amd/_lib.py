@@ -28,8 +28,8 @@ SIGNATURES = {
     "ulysses_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32, _f32, _i32, _vp]),
     "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
-    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
-                        _f32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
+                        _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
     "uly_last_error": (ctypes.c_char_p, []),
     "uly_check_cu_seqlens": (_i32, [ctypes.POINTER(ctypes.c_int32), _i32, _i64]),
 }
@@ -160,20 +160,22 @@ def attn_bwd_workspace_size(N: int, hq: int, hk: int, D: int, dtype) -> int:
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, cu_seqlens=None,
              causal: int = 1, stream=None) -> None:
-    """Gradients dq, dk, dv of sum(dout * o) (see include/ulysses.h)."""
+    """Gradients dq, dk, dv of sum(dout * o) (see include/ulysses.h). The
+    gradient type (grad_dt) is taken from dq: the input type, or float32."""
     import torch
     N, hq, D = q.shape
     hk = k.shape[1]
     dt = q.dtype
+    gdt = dq.dtype
     args = [_dev(q, (N, hq, D), dt, "q"), _dev(k, (N, hk, D), dt, "k"), _dev(v, (N, hk, D), dt, "v"),
             _dev(o, (N, hq, D), dt, "o"), _dev(dout, (N, hq, D), dt, "dout"),
-            _dev(lse, (hq, N), torch.float32, "lse"), _dev(dq, (N, hq, D), dt, "dq"),
-            _dev(dk, (N, hk, D), dt, "dk"), _dev(dv, (N, hk, D), dt, "dv")]
+            _dev(lse, (hq, N), torch.float32, "lse"), _dev(dq, (N, hq, D), gdt, "dq"),
+            _dev(dk, (N, hk, D), gdt, "dk"), _dev(dv, (N, hk, D), gdt, "dv")]
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     cu, nd = _cu(cu_seqlens, N)
-    _raise(lib().attn_bwd(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
+    _raise(lib().attn_bwd(*args, N, hq, hk, D, _dtype_code(q), _dtype_code(dq), cu, nd, float(softmax_scale), int(causal),
                           ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream)))
 
 

@@ -152,11 +152,14 @@ uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype d
 
 uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
-                    uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                    uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale,
+                    int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   uly::AttnDesc d;
   uly_status s = check_attn("attn_bwd", N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
   if (s != ULY_OK) return s;
+  CHECK(valid_dtype(grad_dt), ULY_ERR_INVALID_ARG, "attn_bwd: unknown grad_dt %d", (int)grad_dt);
+  CHECK(grad_dt == dt || grad_dt == ULY_F32, ULY_ERR_UNSUPPORTED,
+        "attn_bwd: grad_dt must equal dt or be ULY_F32", 0);
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 9; ++i)
@@ -167,7 +170,8 @@ uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o, 
         workspace_bytes, need);
   CHECK(need == 0 || (workspace != nullptr && aligned16(workspace)), ULY_ERR_INVALID_ARG,
         "attn_bwd: workspace is NULL or not 16-byte aligned");
-  return from_hip(uly::launch_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream), "attn_bwd");
+  return from_hip(uly::launch_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, grad_dt, stream),
+                  "attn_bwd");
 }
 
 }  // extern "C"

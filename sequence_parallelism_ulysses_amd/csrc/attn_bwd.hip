@@ -1,13 +1,664 @@
-// Attention backward: not yet implemented (placeholder so the library links).
+// Causal GQA / packed-document attention backward for one head group.
+//
+// Gradients of L = sum(dO * O) for O = softmax(scale * Q K^T + mask) V, with
+// the probabilities recomputed from the forward's log-sum-exp (training runs
+// the attention step forward and backward; "Ulysses Sequence Parallelism:
+// Training with Million-Token Contexts"):
+//   delta_i = dO_i . O_i
+//   P_ij = exp(scale q_i.k_j - lse_i),   dP_ij = dO_i . v_j,
+//   dS_ij = P_ij (dP_ij - delta_i)
+//   dV_j = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
+//
+// Three kernels, all deterministic (no atomics):
+//   1. delta: one row dot product per (query, head).
+//   2. dK/dV, key-stationary: a workgroup owns 128 keys of one kv head (32 per
+//      wave, K and V held in registers), walks the query tiles that can see
+//      them for every q head of the group, and sums the GQA heads in its
+//      accumulators. Per wave and 64-query tile:
+//        S  = Q K^T, dP = dO V^T   (A operand: Q/dO rows from LDS)
+//        dV^T += dO^T P, dK^T += Q^T dS   (A operand: transposed Q/dO tiles)
+//      The S/dP accumulators hold one key column per lane, which is exactly
+//      the B-operand layout the second pair of products needs.
+//   3. dQ, query-stationary: like the forward, a wave owns 32 query rows and
+//      walks the key tiles: S^T = K Q^T, dP^T = V dO^T, then
+//      dQ^T += K^T dS^T from a transposed K tile.
+//
+// LDS tiles (bf16) are stored twice, row-major and transposed, from one
+// global load. Both layouts use an XOR swizzle of the 16-byte chunk index so
+// that MFMA operand reads (8 consecutive rows per access phase) and the
+// transposing stores stay bank-conflict free or nearly so.
+#include <cmath>
+#include <numeric>
+
+#include "common.hpp"
 #include "internal.hpp"
 
 namespace uly {
+namespace {
 
-size_t bwd_workspace_bytes(const AttnDesc& d) { return size_t(4) * d.hq * d.N; }
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int BT = 64;  // rows of a staged Q/dO tile (dK/dV) or K/V tile (dQ)
 
-hipError_t launch_attn_bwd(const void*, const void*, const void*, const void*, const void*, const float*,
-                           void*, void*, void*, void*, const AttnDesc&, hipStream_t) {
-  return hipErrorNotSupported;
+struct BwdParams {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* o;
+  const char* dout;
+  const float* lse;
+  char* dq;
+  char* dk;
+  char* dv;
+  float* delta;
+  const int32_t* cu;
+  int ndocs;
+  int N, hq, hk, G, Gw;
+  int n_tiles;
+  float scale, scale_log2;
+};
+
+// ----------------------------------------------------------------------------
+// LDS layouts for bf16 tiles of BT rows x D columns.
+//   row-major   : row r at r*2D bytes, 16-byte chunk c stored at chunk c ^ (r & 7)
+//   transposed  : column d at d*2BT bytes; rows (tokens) in the order of
+//                 tr_slot() inside each 16-row group, 16-byte chunk c stored
+//                 at chunk c ^ swz(d)
+// ----------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int rm_off(int row, int chunk) {
+  return row * (2 * D) + ((chunk ^ (row & 7)) << 4);
+}
+__device__ __forceinline__ int swz(int d) { return (d ^ (d >> 3)) & 7; }
+__device__ __forceinline__ int tr_off(int d, int slot) {
+  return d * (2 * BT) + ((((slot >> 3) ^ swz(d))) << 4) + ((slot & 7) << 1);
+}
+// Position of token group g (4 consecutive tokens) inside the transposed tile:
+// order [0-3, 8-11, 4-7, 12-15] per 16 tokens, so that half-wave h reads the
+// tokens {4h..4h+3, 8+4h..8+4h+3} its accumulator-derived fragment holds.
+__device__ __forceinline__ int tr_slot(int g) {
+  const int sub = g & 3;
+  return (g >> 2) * 16 + ((sub & 1) << 3) + ((sub >> 1) << 2);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+// Store 4 consecutive gradient values as fp32 (16 bytes) or bf16 (8 bytes,
+// rounded to nearest even).
+template <bool kF32>
+__device__ __forceinline__ void store4(char* dst, const float (&x)[4]) {
+  if constexpr (kF32) {
+    *reinterpret_cast<u32x4_t*>(dst) =
+        u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  } else {
+    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  }
+}
+
+// Transposing store of a 4-token x 8-column block (x[i] = token 4g+i, columns
+// 8dc..8dc+7) into the transposed layout.
+__device__ __forceinline__ void store_tr(char* base, const u32x4_t (&x)[4], int g, int dc) {
+  const int slot = tr_slot(g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w0 = x[0][j], w1 = x[1][j], w2 = x[2][j], w3 = x[3][j];
+    const u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+    const u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
+    *reinterpret_cast<u32x2_t*>(base + tr_off(dc * 8 + 2 * j, slot)) = lo;
+    *reinterpret_cast<u32x2_t*>(base + tr_off(dc * 8 + 2 * j + 1, slot)) = hi;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 1. delta_i = dO_i . O_i  (fp32), for every (query, head). Each lane reads
+//    16 bytes of the row, so a row takes D*E/16 lanes (8..32).
+// ----------------------------------------------------------------------------
+template <class Tr, int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel(BwdParams p) {
+  constexpr int E = Tr::kElem;
+  constexpr int LPR = D * E / 16;  // lanes per row
+  static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row split");
+  const int64_t row = int64_t(blockIdx.x) * (kThreads / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  const int64_t rows = int64_t(p.N) * p.hq;
+  float acc = 0.f;
+  if (row < rows) {
+    const int64_t off = row * D * E + sub * 16;  // row = q * hq + h
+    const u32x4_t x = ld16(p.o + off), y = ld16(p.dout + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (E == 2) {
+        acc = fmaf(bf16_bits_to_f32(x[j] & 0xffffu), bf16_bits_to_f32(y[j] & 0xffffu), acc);
+        acc = fmaf(bf16_bits_to_f32(x[j] >> 16), bf16_bits_to_f32(y[j] >> 16), acc);
+      } else {
+        acc = fmaf(__uint_as_float(x[j]), __uint_as_float(y[j]), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+  if (row < rows && sub == 0) {
+    const int64_t q = row / p.hq, h = row % p.hq;
+    p.delta[h * p.N + q] = acc;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 2. dK / dV (key-stationary)
+// ----------------------------------------------------------------------------
+template <class Tr, int D>
+struct KvCfg {
+  static constexpr int E = Tr::kElem;
+  static constexpr bool kBf = (E == 2);
+  static constexpr int KS = D / Tr::kStep;   // MFMA steps over D
+  static constexpr int DB = D / 32;
+  static constexpr int QS = BT / Tr::kStep;  // MFMA steps over the 64 queries of a tile
+  static constexpr int DC = D / 8;           // bf16: 8-column chunks per row
+  static constexpr int PAIRS = (BT / 4) * DC;
+  // f32 tiles are row-major with a 16-byte pad per row.
+  static constexpr int F_STRIDE = D * 4 + 16;
+  static constexpr int X_BYTES = kBf ? BT * D * 2 : BT * F_STRIDE;  // one row-major tile
+  static constexpr int T_BYTES = kBf ? BT * D * 2 : 0;              // one transposed tile
+  static constexpr int STAGE = 2 * X_BYTES + 2 * T_BYTES + 2 * BT * 4;
+  static constexpr int F_CH = BT * D * 4 / 16 / kThreads;           // f32 chunks per thread
+  static_assert(!kBf || PAIRS <= kThreads, "one pair per thread at most");
+};
+
+template <class Tr, int D>
+struct QTile {
+  using C = KvCfg<Tr, D>;
+  static constexpr int NR = C::kBf ? 4 : C::F_CH;
+  u32x4_t xq[NR], xd[NR];
+  float lse2, dlt;
+
+  __device__ __forceinline__ void load(const BwdParams& p, int head, int qs, int tid) {
+    const int64_t row_bytes = int64_t(p.hq) * D * C::E;
+    const char* qb = p.q + int64_t(head) * D * C::E;
+    const char* db = p.dout + int64_t(head) * D * C::E;
+    if constexpr (C::kBf) {
+      if (tid < C::PAIRS) {
+        const int dc = tid % C::DC, g = tid / C::DC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = qs + 4 * g + i;
+          const bool ok = q < p.N;
+          xq[i] = ok ? ld16(qb + q * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
+          xd[i] = ok ? ld16(db + q * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int c = tid + kThreads * i;
+        const int row = c / (D / 4), col = c % (D / 4);
+        const int q = qs + row;
+        const bool ok = q < p.N;
+        xq[i] = ok ? ld16(qb + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+        xd[i] = ok ? ld16(db + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+    if (tid < BT) {
+      const int q = qs + tid;
+      lse2 = q < p.N ? p.lse[int64_t(head) * p.N + q] * kLog2e : 0.f;
+      dlt = q < p.N ? p.delta[int64_t(head) * p.N + q] : 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void store(char* st, int tid) const {
+    char* qr = st;
+    char* dr = st + C::X_BYTES;
+    char* qt = st + 2 * C::X_BYTES;
+    char* dt = qt + C::T_BYTES;
+    float* fl = reinterpret_cast<float*>(st + 2 * C::X_BYTES + 2 * C::T_BYTES);
+    if constexpr (C::kBf) {
+      if (tid < C::PAIRS) {
+        const int dc = tid % C::DC, g = tid / C::DC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<u32x4_t*>(qr + rm_off<D>(4 * g + i, dc)) = xq[i];
+          *reinterpret_cast<u32x4_t*>(dr + rm_off<D>(4 * g + i, dc)) = xd[i];
+        }
+        store_tr(qt, xq, g, dc);
+        store_tr(dt, xd, g, dc);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int c = tid + kThreads * i;
+        const int row = c / (D / 4), col = c % (D / 4);
+        *reinterpret_cast<u32x4_t*>(qr + row * C::F_STRIDE + col * 16) = xq[i];
+        *reinterpret_cast<u32x4_t*>(dr + row * C::F_STRIDE + col * 16) = xd[i];
+      }
+    }
+    if (tid < BT) {
+      fl[tid] = lse2;
+      fl[BT + tid] = dlt;
+    }
+  }
+};
+
+template <class Tr, int D, bool kF32Out>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
+  using C = KvCfg<Tr, D>;
+  using frag_t = typename Tr::frag_t;
+  constexpr int E = C::E;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int kvh = blockIdx.y;
+  const int kv0 = int(blockIdx.x) * (32 * kWaves);  // first tiles carry the most causal work
+  const int kw0 = kv0 + 32 * w;
+  const bool active = kw0 < p.N;
+  const int key = kw0 + l32;
+  const int my_de = doc_of(p.cu, p.ndocs, p.N, min(key, p.N - 1)).end;
+  const int w_de_first = doc_of(p.cu, p.ndocs, p.N, min(kw0, p.N - 1)).end;
+  const int w_de_last = doc_of(p.cu, p.ndocs, p.N, min(kw0 + 31, p.N - 1)).end;
+
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
+  frag_t kf[C::KS], vf[C::KS];
+  {
+    const int64_t off = (int64_t(key) * p.hk + kvh) * D * E + half * Tr::kEpl * E;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = key < p.N ? load_frag<Tr>(p.k + off + ks * Tr::kStep * E) : frag_t{};
+      vf[ks] = key < p.N ? load_frag<Tr>(p.v + off + ks * Tr::kStep * E) : frag_t{};
+    }
+  }
+  f32x16_t dkt[C::DB], dvt[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dkt[db] = dvt[db] = f32x16_t{};
+
+  // Queries that can see any of the 128 keys: [kv0, end of the last key's document).
+  const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + 32 * kWaves - 1, p.N - 1)).end;
+  const int qt0 = kv0 / BT, qt1 = (q_end - 1) / BT;
+  const int n_it = (qt1 - qt0 + 1) * p.G;
+
+  QTile<Tr, D> tile;
+  tile.load(p, kvh * p.G, qt0 * BT, tid);
+  tile.store(smem, tid);
+  __syncthreads();
+  if (n_it > 1) tile.load(p, kvh * p.G + 1 % p.G, (qt0 + 1 / p.G) * BT, tid);
+
+  for (int it = 0; it < n_it; ++it) {
+    const int qs = (qt0 + it / p.G) * BT;
+    const char* st = smem + (it & 1) * C::STAGE;
+    const char* qr = st;
+    const char* dr = st + C::X_BYTES;
+    const char* qt = st + 2 * C::X_BYTES;
+    const char* dt = qt + C::T_BYTES;
+    const float* fl = reinterpret_cast<const float*>(st + 2 * C::X_BYTES + 2 * C::T_BYTES);
+
+    if (active && qs + BT - 1 >= kw0 && qs < w_de_last) {
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int row = qb * 32 + l32;
+          frag_t a, b;
+          if constexpr (C::kBf) {
+            a = load_frag<Tr>(qr + rm_off<D>(row, 2 * ks + half));
+            b = load_frag<Tr>(dr + rm_off<D>(row, 2 * ks + half));
+          } else {
+            a = load_frag<Tr>(qr + row * C::F_STRIDE + (2 * ks + half) * 4);
+            b = load_frag<Tr>(dr + row * C::F_STRIDE + (2 * ks + half) * 4);
+          }
+          s[qb] = mfma(a, kf[ks], s[qb]);
+          dp[qb] = mfma(b, vf[ks], dp[qb]);
+        }
+      }
+      const bool need_mask = (qs < kw0 + 31) || (qs + BT > w_de_first);
+      float pv[32], dsv[32];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi = qb * 32 + 8 * r4 + 4 * half;  // first of 4 consecutive queries
+          const float4 l4 = *reinterpret_cast<const float4*>(fl + qi);
+          const float4 d4 = *reinterpret_cast<const float4*>(fl + BT + qi);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * r4 + j;
+            float e = fast_exp2(fmaf(s[qb][r], p.scale_log2, -lv[j]));
+            if (need_mask) {
+              const int q = qs + qi + j;
+              if (q < key || q >= my_de) e = 0.f;
+            }
+            pv[qb * 16 + r] = e;
+            dsv[qb * 16 + r] = e * (dp[qb][r] - dv4[j]);
+          }
+        }
+      // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the tile's queries)
+#pragma unroll
+      for (int st2 = 0; st2 < C::QS; ++st2) {
+        const frag_t pf = make_frag<Tr>(&pv[st2 * Tr::kEpl]);
+        const frag_t sf = make_frag<Tr>(&dsv[st2 * Tr::kEpl]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int d = db * 32 + l32;
+          frag_t ad, aq;
+          if constexpr (C::kBf) {
+            ad = load_frag<Tr>(dt + tr_off(d, st2 * 16 + half * 8));
+            aq = load_frag<Tr>(qt + tr_off(d, st2 * 16 + half * 8));
+          } else {
+            const int qrow = (st2 >> 4) * 32 + acc_row(st2 & 15, half);
+            ad = load_frag<Tr>(dr + qrow * C::F_STRIDE + d * 4);
+            aq = load_frag<Tr>(qr + qrow * C::F_STRIDE + d * 4);
+          }
+          dvt[db] = mfma(ad, pf, dvt[db]);
+          dkt[db] = mfma(aq, sf, dkt[db]);
+        }
+      }
+    }
+
+    if (it + 1 < n_it) {
+      tile.store(smem + ((it + 1) & 1) * C::STAGE, tid);
+      if (it + 2 < n_it) {
+        const int nx = it + 2;
+        tile.load(p, kvh * p.G + nx % p.G, (qt0 + nx / p.G) * BT, tid);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: lane (key, half) holds d = 32 db + acc_row(r, half).
+  if (active && key < p.N) {
+    constexpr int OE = kF32Out ? 4 : 2;
+    const int64_t off = (int64_t(key) * p.hk + kvh) * D * OE;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + 8 * r4 + 4 * half;
+        float kx[4], vx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[j] = dkt[db][4 * r4 + j] * p.scale;
+          vx[j] = dvt[db][4 * r4 + j];
+        }
+        store4<kF32Out>(p.dk + off + d * OE, kx);
+        store4<kF32Out>(p.dv + off + d * OE, vx);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 3. dQ (query-stationary)
+// ----------------------------------------------------------------------------
+template <class Tr, int D>
+struct QCfg {
+  static constexpr int E = Tr::kElem;
+  static constexpr bool kBf = (E == 2);
+  static constexpr int KS = D / Tr::kStep;
+  static constexpr int DB = D / 32;
+  static constexpr int PV = BT / Tr::kStep;
+  static constexpr int DC = D / 8;
+  static constexpr int PAIRS = (BT / 4) * DC;
+  static constexpr int F_STRIDE = D * 4 + 16;
+  static constexpr int X_BYTES = kBf ? BT * D * 2 : BT * F_STRIDE;
+  static constexpr int T_BYTES = kBf ? BT * D * 2 : 0;
+  static constexpr int STAGE = 2 * X_BYTES + T_BYTES;  // K row-major, V row-major, K transposed
+  static constexpr int F_CH = BT * D * 4 / 16 / kThreads;
+};
+
+template <class Tr, int D>
+struct KvTile {
+  using C = QCfg<Tr, D>;
+  static constexpr int NR = C::kBf ? 4 : C::F_CH;
+  u32x4_t xk[NR], xv[NR];
+
+  __device__ __forceinline__ void load(const BwdParams& p, int kvh, int kv0, int tid) {
+    const int64_t row_bytes = int64_t(p.hk) * D * C::E;
+    const char* kb = p.k + int64_t(kvh) * D * C::E;
+    const char* vb = p.v + int64_t(kvh) * D * C::E;
+    if constexpr (C::kBf) {
+      if (tid < C::PAIRS) {
+        const int dc = tid % C::DC, g = tid / C::DC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kv0 + 4 * g + i;
+          const bool ok = key < p.N;
+          xk[i] = ok ? ld16(kb + key * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
+          xv[i] = ok ? ld16(vb + key * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int c = tid + kThreads * i;
+        const int row = c / (D / 4), col = c % (D / 4);
+        const int key = kv0 + row;
+        const bool ok = key < p.N;
+        xk[i] = ok ? ld16(kb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+        xv[i] = ok ? ld16(vb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(char* st, int tid) const {
+    char* kr = st;
+    char* vr = st + C::X_BYTES;
+    char* kt = st + 2 * C::X_BYTES;
+    if constexpr (C::kBf) {
+      if (tid < C::PAIRS) {
+        const int dc = tid % C::DC, g = tid / C::DC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<u32x4_t*>(kr + rm_off<D>(4 * g + i, dc)) = xk[i];
+          *reinterpret_cast<u32x4_t*>(vr + rm_off<D>(4 * g + i, dc)) = xv[i];
+        }
+        store_tr(kt, xk, g, dc);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int c = tid + kThreads * i;
+        const int row = c / (D / 4), col = c % (D / 4);
+        *reinterpret_cast<u32x4_t*>(kr + row * C::F_STRIDE + col * 16) = xk[i];
+        *reinterpret_cast<u32x4_t*>(vr + row * C::F_STRIDE + col * 16) = xv[i];
+      }
+    }
+  }
+};
+
+template <class Tr, int D, bool kF32Out>
+__global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
+  using C = QCfg<Tr, D>;
+  using frag_t = typename Tr::frag_t;
+  constexpr int E = C::E;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int groups = p.G / p.Gw;
+  const int kvh = blockIdx.y / groups, sub = blockIdx.y % groups;
+  const int QW = kWaves / p.Gw;
+  const int qtile = p.n_tiles - 1 - int(blockIdx.x);  // heaviest first
+  const int wg_q0 = qtile * 32 * QW;
+  const int wg_q1 = min(p.N, wg_q0 + 32 * QW);
+  const int head = kvh * p.G + sub * p.Gw + (w % p.Gw);
+  const int qbase = wg_q0 + (w / p.Gw) * 32;
+  const bool active = qbase < p.N;
+  const int wq_last = min(qbase + 31, p.N - 1);
+  const int my_q = qbase + l32;
+  const int my_ds = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1)).start;
+  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
+  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+  const bool q_ok = my_q < p.N;
+  const float my_lse2 = q_ok ? p.lse[int64_t(head) * p.N + my_q] * kLog2e : 0.f;
+  const float my_dlt = q_ok ? p.delta[int64_t(head) * p.N + my_q] : 0.f;
+
+  frag_t qf[C::KS], df[C::KS];
+  {
+    const int64_t off = (int64_t(my_q) * p.hq + head) * D * E + half * Tr::kEpl * E;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      qf[ks] = q_ok ? load_frag<Tr>(p.q + off + ks * Tr::kStep * E) : frag_t{};
+      df[ks] = q_ok ? load_frag<Tr>(p.dout + off + ks * Tr::kStep * E) : frag_t{};
+    }
+  }
+  f32x16_t dqt[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dqt[db] = f32x16_t{};
+
+  const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
+  const int t0 = kv_begin / BT, t1 = (wg_q1 - 1) / BT;
+
+  KvTile<Tr, D> tile;
+  tile.load(p, kvh, t0 * BT, tid);
+  tile.store(smem, tid);
+  __syncthreads();
+  if (t0 + 1 <= t1) tile.load(p, kvh, (t0 + 1) * BT, tid);
+
+  for (int t = t0; t <= t1; ++t) {
+    const int kv0 = t * BT;
+    const char* st = smem + ((t - t0) & 1) * C::STAGE;
+    const char* kr = st;
+    const char* vr = st + C::X_BYTES;
+    const char* kt = st + 2 * C::X_BYTES;
+
+    if (active && kv0 <= wq_last && kv0 + BT > w_ds_first) {
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + l32;
+          frag_t a, b;
+          if constexpr (C::kBf) {
+            a = load_frag<Tr>(kr + rm_off<D>(row, 2 * ks + half));
+            b = load_frag<Tr>(vr + rm_off<D>(row, 2 * ks + half));
+          } else {
+            a = load_frag<Tr>(kr + row * C::F_STRIDE + (2 * ks + half) * 4);
+            b = load_frag<Tr>(vr + row * C::F_STRIDE + (2 * ks + half) * 4);
+          }
+          s[kb] = mfma(a, qf[ks], s[kb]);
+          dp[kb] = mfma(b, df[ks], dp[kb]);
+        }
+      }
+      const bool need_mask = (kv0 + BT - 1 > qbase) || (kv0 < w_ds_last);
+      float dsv[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
+          if (need_mask) {
+            const int key = kv0 + kb * 32 + acc_row(r, half);
+            if (key > my_q || key < my_ds) e = 0.f;
+          }
+          dsv[kb * 16 + r] = e * (dp[kb][r] - my_dlt);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int st2 = 0; st2 < C::PV; ++st2) {
+        const frag_t sf = make_frag<Tr>(&dsv[st2 * Tr::kEpl]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int d = db * 32 + l32;
+          frag_t a;
+          if constexpr (C::kBf) {
+            a = load_frag<Tr>(kt + tr_off(d, st2 * 16 + half * 8));
+          } else {
+            const int krow = (st2 >> 4) * 32 + acc_row(st2 & 15, half);
+            a = load_frag<Tr>(kr + krow * C::F_STRIDE + d * 4);
+          }
+          dqt[db] = mfma(a, sf, dqt[db]);
+        }
+      }
+    }
+
+    if (t + 1 <= t1) {
+      tile.store(smem + ((t + 1 - t0) & 1) * C::STAGE, tid);
+      if (t + 2 <= t1) tile.load(p, kvh, (t + 2) * BT, tid);
+    }
+    __syncthreads();
+  }
+
+  if (active && q_ok) {
+    constexpr int OE = kF32Out ? 4 : 2;
+    char* dst = p.dq + (int64_t(my_q) * p.hq + head) * D * OE;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + 8 * r4 + 4 * half;
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = dqt[db][4 * r4 + j] * p.scale;
+        store4<kF32Out>(dst + d * OE, x);
+      }
+  }
+}
+
+template <class Tr, int D, bool kF32Out>
+hipError_t launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, void* workspace, const AttnDesc& d, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const char*>(q);
+  p.k = static_cast<const char*>(k);
+  p.v = static_cast<const char*>(v);
+  p.o = static_cast<const char*>(o);
+  p.dout = static_cast<const char*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<char*>(dq);
+  p.dk = static_cast<char*>(dk);
+  p.dv = static_cast<char*>(dv);
+  p.delta = static_cast<float*>(workspace);
+  p.cu = d.cu;
+  p.ndocs = d.ndocs;
+  p.N = static_cast<int>(d.N);
+  p.hq = d.hq;
+  p.hk = d.hk;
+  p.G = d.hq / d.hk;
+  p.Gw = std::gcd(p.G, kWaves);
+  p.scale = d.scale;
+  p.scale_log2 = d.scale * kLog2e;
+
+  const int64_t rows = d.N * d.hq;
+  const int64_t rows_per_block = kThreads / (D * Tr::kElem / 16);
+  delta_kernel<Tr, D><<<dim3(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block)), kThreads, 0,
+                        stream>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  p.n_tiles = static_cast<int>((d.N + 32 * kWaves - 1) / (32 * kWaves));
+  dkdv_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles, d.hk), kThreads, 0, stream>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int rows_per_wg = 32 * (kWaves / p.Gw);
+  p.n_tiles = static_cast<int>((d.N + rows_per_wg - 1) / rows_per_wg);
+  dq_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles, d.hk * (p.G / p.Gw)), kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const AttnDesc& d) {
+  const size_t delta = size_t(4) * size_t(d.hq) * size_t(d.N);
+  return (delta + 255) & ~size_t(255);
+}
+
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, void* workspace, const AttnDesc& d,
+                           uly_dtype grad_dt, hipStream_t stream) {
+  if (d.dt == ULY_BF16) {
+    if (grad_dt == ULY_F32)
+      return d.D == 128 ? launch<TrBF16, 128, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream)
+                        : launch<TrBF16, 64, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream);
+    return d.D == 128 ? launch<TrBF16, 128, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream)
+                      : launch<TrBF16, 64, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream);
+  }
+  return d.D == 128 ? launch<TrF32, 128, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream)
+                    : launch<TrF32, 64, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, stream);
 }
 
 }  // namespace uly

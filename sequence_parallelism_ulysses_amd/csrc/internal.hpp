@@ -39,6 +39,6 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
 size_t bwd_workspace_bytes(const AttnDesc& d);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           void* workspace, const AttnDesc& d, hipStream_t stream);
+                           void* workspace, const AttnDesc& d, uly_dtype grad_dt, hipStream_t stream);
 
 }  // namespace uly

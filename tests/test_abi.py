@@ -116,10 +116,11 @@ def test_attn_fwd_rejects(kw, status, needle):
 
 def _bwd(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, N=1024, hq=4, hk=1,
-             D=128, dt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, ws=FAKE, wsb=1 << 30, stream=None)
+             D=128, dt=uly.ULY_BF16, gdt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, ws=FAKE, wsb=1 << 30,
+             stream=None)
     a.update(kw)
     return uly.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["N"],
-                              a["hq"], a["hk"], a["D"], a["dt"], a["cu"], a["nd"], a["scale"], a["causal"], a["ws"],
+                              a["hq"], a["hk"], a["D"], a["dt"], a["gdt"], a["cu"], a["nd"], a["scale"], a["causal"], a["ws"],
                               a["wsb"], a["stream"])
 
 
@@ -131,6 +132,8 @@ def _bwd(**kw):
     (dict(causal=0), uly.ULY_ERR_UNSUPPORTED, "causal"),
     (dict(D=256), uly.ULY_ERR_INVALID_ARG, "D=256"),
     (dict(N=-5), uly.ULY_ERR_INVALID_ARG, "N=-5"),
+    (dict(gdt=5), uly.ULY_ERR_INVALID_ARG, "grad_dt"),
+    (dict(dt=uly.ULY_F32, gdt=uly.ULY_BF16), uly.ULY_ERR_UNSUPPORTED, "grad_dt"),
 ])
 def test_attn_bwd_rejects(kw, status, needle):
     assert _bwd(**kw) == status

@@ -1,0 +1,193 @@
+"""GPU parity of attn_bwd (and the whole pack -> fwd -> bwd -> unpack path)
+against the fp64 oracle.
+
+Tolerances:
+  - fp32 workload: max-abs <= 1e-4.
+  - bf16 inputs: the gradients are computed once more with fp32 outputs
+    (grad_dt = fp32, the same arithmetic stored before the final rounding);
+    those must be within max-abs 2e-2 of the oracle, and the bf16 gradients
+    must equal their round-to-nearest-even bit for bit. So every bf16
+    gradient is within 2e-2 plus half a bf16 ulp of the exact value; the
+    final rounding alone can cost half an ulp (0.0078 at |x| in [2, 4)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import sequence_parallelism_ulysses_amd as uly
+import synthetic as syn
+from oracle import attn_ref, unpack_ref
+from harness import (DEV, Run, assert_close, bf16_tol, decode, dev_to_bits, oracle_attention, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(run, grad_f32=None):
+    """pack -> fwd -> bwd. For bf16 inputs the backward runs twice, with bf16
+    and with fp32 gradient outputs (keys dq/dk/dv and dq32/dk32/dv32)."""
+    c = run.cfg
+    q, k, v, do = run.packed("q"), run.packed("k"), run.packed("v"), run.packed("do")
+    o = torch.empty_like(q)
+    lse = torch.empty((c.hq, c.N), dtype=torch.float32, device=DEV)
+    uly.attn_fwd(q, k, v, o, lse, c.scale, run.cu_dev)
+    ws = torch.empty(uly.attn_bwd_workspace_size(c.N, c.hq, c.hk, c.D, q.dtype), dtype=torch.uint8, device=DEV)
+    out = dict(o=o, lse=lse)
+    kinds = [("", q.dtype)] + ([("32", torch.float32)] if q.dtype == torch.bfloat16 and grad_f32 is not False else [])
+    for suffix, gdt in kinds:
+        dq = torch.full(q.shape, float("nan"), dtype=gdt, device=DEV)
+        dk = torch.full(k.shape, float("nan"), dtype=gdt, device=DEV)
+        dv = torch.full(v.shape, float("nan"), dtype=gdt, device=DEV)
+        uly.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, c.scale, ws, run.cu_dev)
+        out.update({"dq" + suffix: dq, "dk" + suffix: dk, "dv" + suffix: dv})
+    torch.cuda.synchronize()
+    return out
+
+
+def tol_for(cfg, ref):
+    return 1e-4 if cfg.dtype == "f32" else bf16_tol(ref)
+
+
+def _rne_bits(t32):
+    return dev_to_bits(t32.to(torch.bfloat16))
+
+
+def check_grad(cfg, got, ref_vals, name, sel=slice(None), ref_sel=slice(None)):
+    """One gradient tensor against the oracle, on rows `sel` of the GPU result
+    and `ref_sel` of the oracle's."""
+    ref = ref_vals[name][ref_sel]
+    if cfg.dtype == "f32":
+        assert_close(decode(dev_to_bits(got[name][sel])), ref, 1e-4, name)
+        return
+    g32 = got[name + "32"][sel]
+    assert_close(g32.cpu().numpy().astype(np.float64), ref, 2e-2, name + " (fp32 out)")
+    assert np.array_equal(dev_to_bits(got[name][sel]), _rne_bits(g32)), name + ": bf16 != RNE(fp32)"
+
+
+def check_grads(cfg, got, ref, rows=None, key_cols=None):
+    sel_r = slice(None) if rows is None else torch.from_numpy(rows).to(DEV)
+    check_grad(cfg, got, ref, "dq", sel=sel_r)
+    sel_k = slice(None) if key_cols is None else slice(key_cols, None)
+    for name in ("dk", "dv"):
+        check_grad(cfg, got, ref, name, sel=sel_k, ref_sel=sel_k)
+
+
+def test_bwd_c1_fp32_full():
+    cfg = syn.CONFIGS["c1"]
+    run = Run(cfg)
+    got = run_fwd_bwd(run)
+    check_grads(cfg, got, oracle_attention(run))
+
+
+SMALL = [
+    (1000, 8, 32, 8, 128, "bf16", None),
+    (3000, 8, 32, 8, 128, "bf16", [1, 700, 0, 129, 1000, 1170]),
+    (777, 7, 14, 14, 64, "bf16", None),
+    (512, 4, 32, 8, 128, "bf16", [64, 64, 128, 256]),
+    (300, 2, 12, 4, 128, "bf16", [150, 150]),
+    (333, 3, 6, 3, 128, "f32", None),
+    (64, 1, 4, 1, 64, "f32", [10, 54]),
+    (8, 8, 8, 8, 128, "bf16", None),
+    (200, 2, 4, 2, 64, "f32", [33, 0, 167]),
+]
+
+
+@pytest.mark.parametrize("N,P,Hq,Hkv,D,dtype,lens", SMALL)
+def test_bwd_small_full(N, P, Hq, Hkv, D, dtype, lens):
+    cfg = syn.custom(N, P, Hq, Hkv, D, dtype, seed=7 * N + D)
+    cu = None if lens is None else syn.cu_from_lengths(lens)
+    run = Run(cfg, cu=cu)
+    got = run_fwd_bwd(run)
+    check_grads(cfg, got, oracle_attention(run))
+
+
+def test_bwd_c5_packed_documents_full():
+    cfg = syn.CONFIGS["c5"]
+    run = Run(cfg)
+    got = run_fwd_bwd(run)
+    ref = oracle_attention(run)
+    check_grads(cfg, got, ref)
+    assert_close(decode(dev_to_bits(got["o"])), ref["o"], bf16_tol(ref["o"]), "O")
+    assert_close(got["lse"].cpu().numpy().astype(np.float64), ref["lse"], 1e-3, "LSE")
+
+
+def test_bwd_c2_full():
+    """Llama-3.1-8B-shaped head group at 32k tokens, every gradient element."""
+    cfg = syn.CONFIGS["c2"]
+    run = Run(cfg)
+    got = run_fwd_bwd(run)
+    check_grads(cfg, got, oracle_attention(run))
+
+
+def test_bwd_c3_sampled_rows_and_tail_columns():
+    """128k tokens: dQ on sampled rows; dK/dV exactly on the last 1024 key
+    columns (only rows >= N-1024 reach them); document sum rules overall."""
+    cfg = syn.CONFIGS["c3"]
+    run = Run(cfg)
+    got = run_fwd_bwd(run)
+    rows = sample_rows(cfg.N, None, n_random=48)
+    tail = cfg.N - 1024
+    ref_rows = oracle_attention(run, rows=rows)
+    check_grad(cfg, got, ref_rows, "dq", sel=torch.from_numpy(rows).to(DEV))
+    ref_tail = oracle_attention(run, rows=np.arange(tail, cfg.N))
+    for name in ("dk", "dv"):
+        check_grad(cfg, got, ref_tail, name, sel=slice(tail, None), ref_sel=slice(tail, None))
+    # sum rules over the whole (single) document, a check of every column at
+    # once: sum_j dK_j = 0 and sum_j dV_j = sum over heads and rows of dO.
+    # Bound: 1% of the summed magnitudes (rounding of bf16 outputs and of the
+    # bf16 P/dS operands leaves a residue far below that; a dropped or doubled
+    # query tile does not).
+    dk = decode(dev_to_bits(got["dk"]))[:, 0]
+    dv = decode(dev_to_bits(got["dv"]))[:, 0]
+    do = decode(dev_to_bits(run.packed("do")))
+    rk = np.abs(dk.sum(axis=0)) / np.abs(dk).sum(axis=0)
+    rv = np.abs(dv.sum(axis=0) - do.sum(axis=(0, 1))) / np.abs(dv).sum(axis=0)
+    print(f"sum rules: max |sum dK|/sum|dK| = {rk.max():.3g}, max |sum dV - sum dO|/sum|dV| = {rv.max():.3g}")
+    assert rk.max() < 1e-2 and rv.max() < 1e-2
+
+
+def test_full_path_unpack_c1_and_varlen():
+    """pack -> fwd -> bwd -> unpack into canary-filled shards: the unpacked
+    shards equal the oracle's unpack of the GPU's packed outputs bit for bit,
+    and the values match the oracle's attention."""
+    for cfg, cu in ((syn.CONFIGS["c1"], None),
+                    (syn.custom(1024, 4, 16, 8, 128, "bf16", group=3, seed=5), syn.cu_from_lengths([300, 1, 723]))):
+        run = Run(cfg, cu=cu)
+        got = run_fwd_bwd(run, grad_f32=False)
+        ref = oracle_attention(run)
+        for name, heads in (("o", cfg.Hq), ("dq", cfg.Hq), ("dk", cfg.Hkv), ("dv", cfg.Hkv)):
+            canary_val = 1234.5
+            shards = [torch.full((cfg.T, heads, cfg.D), canary_val, dtype=got[name].dtype, device=DEV)
+                      for _ in range(cfg.P)]
+            uly.ulysses_unpack(got[name], cfg.group, shards)
+            torch.cuda.synchronize()
+            host_canary = dev_to_bits(torch.full((cfg.T, heads, cfg.D), canary_val, dtype=got[name].dtype))
+            want = unpack_ref(dev_to_bits(got[name]), [host_canary] * cfg.P, cfg.group)
+            for j in range(cfg.P):
+                assert np.array_equal(dev_to_bits(shards[j]), want[j]), (name, j)
+            val = decode(dev_to_bits(got[name]))
+            # bf16 values: within 2e-2 plus half an ulp (see the module docstring)
+            tol = 1e-4 if cfg.dtype == "f32" else 2e-2 + bf16_tol(ref[name], 0.0) / 2
+            assert_close(val, ref[name], tol, name)
+
+
+def test_bwd_deterministic():
+    """No atomics: two runs give identical bits."""
+    cfg = syn.custom(2048, 8, 32, 8, 128, "bf16", seed=99)
+    run = Run(cfg, cu=syn.cu_from_lengths([1000, 48, 1000]))
+    a = run_fwd_bwd(run)
+    b = run_fwd_bwd(run)
+    for name in ("o", "lse", "dq", "dk", "dv", "dq32", "dk32", "dv32"):
+        assert torch.equal(a[name].view(torch.int16) if a[name].dtype == torch.bfloat16 else a[name],
+                           b[name].view(torch.int16) if b[name].dtype == torch.bfloat16 else b[name]), name
+
+
+def test_bwd_rejects_small_workspace():
+    cfg = syn.custom(64, 1, 4, 1, 128, "bf16")
+    run = Run(cfg)
+    q, k, v, do = run.packed("q"), run.packed("k"), run.packed("v"), run.packed("do")
+    o = torch.empty_like(q)
+    lse = torch.empty((4, 64), dtype=torch.float32, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(uly.UlyssesError) as e:
+        uly.attn_bwd(q, k, v, o, do, lse, torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), cfg.scale, ws)
+    assert e.value.status == uly.ULY_ERR_INVALID_ARG
