@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{path} is missing: the HIP library must be built (python -c "
                 "'import __graft_entry__ as g; g.build()'); there is no fallback path")
+        # torch ships its own HIP runtime with the same soname as ROCm's. Load
+        # torch first so this library binds to that already-loaded runtime;
+        # loading ours first would put two HIP runtimes in the process.
+        import torch  # noqa: F401
         cdll = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(cdll, name)
