@@ -51,12 +51,40 @@ struct BwdParams {
   char* dk;
   char* dv;
   float* delta;
+  float* part_dk;  // [splits][N][hk][D] fp32, when splits > 1
+  float* part_dv;
   const int32_t* cu;
   int ndocs;
   int N, hq, hk, G, Gw;
   int n_tiles;
+  int splits;  // workgroups sharing one dK/dV key tile
   float scale, scale_log2;
 };
+
+constexpr int kKeysPerWg = 32 * kWaves;
+
+// Workgroups per dK/dV key tile: enough that the grid holds about 2048
+// workgroups (8 per CU), so the causal spread of work per key tile (1 to
+// N/64 query tiles) balances across CUs; at most 8.
+int dkdv_splits(const AttnDesc& d) {
+  const int64_t tiles = (d.N + kKeysPerWg - 1) / kKeysPerWg * d.hk;
+  const int64_t want = (2048 + tiles - 1) / tiles;
+  return int(want < 1 ? 1 : (want > 8 ? 8 : want));
+}
+
+struct WsLayout {
+  size_t delta, part, total;
+};
+WsLayout ws_layout(const AttnDesc& d) {
+  WsLayout w;
+  w.delta = 0;
+  const size_t delta_bytes = (size_t(4) * d.hq * d.N + 255) & ~size_t(255);
+  w.part = delta_bytes;
+  const int s = dkdv_splits(d);
+  const size_t part_bytes = s > 1 ? size_t(2) * s * d.N * d.hk * d.D * 4 : 0;
+  w.total = delta_bytes + part_bytes;
+  return w;
+}
 
 // ----------------------------------------------------------------------------
 // LDS layouts for bf16 tiles of BT rows x D columns.
@@ -247,7 +275,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int kvh = blockIdx.y;
-  const int kv0 = int(blockIdx.x) * (32 * kWaves);  // first tiles carry the most causal work
+  const int split = int(blockIdx.x) % p.splits;
+  const int kv0 = (int(blockIdx.x) / p.splits) * (32 * kWaves);  // first tiles carry the most causal work
   const int kw0 = kv0 + 32 * w;
   const bool active = kw0 < p.N;
   const int key = kw0 + l32;
@@ -269,20 +298,29 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dkt[db] = dvt[db] = f32x16_t{};
 
-  // Queries that can see any of the 128 keys: [kv0, end of the last key's document).
+  // Queries that can see any of the 128 keys: [kv0, end of the last key's
+  // document). The (q head, query tile) iterations over them, head-major, are
+  // split evenly between p.splits workgroups; this one takes [it0, it1).
   const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + 32 * kWaves - 1, p.N - 1)).end;
-  const int qt0 = kv0 / BT, qt1 = (q_end - 1) / BT;
-  const int n_it = (qt1 - qt0 + 1) * p.G;
+  const int qt0 = kv0 / BT;
+  const int n_qt = (q_end - 1) / BT - qt0 + 1;
+  const int n_it = n_qt * p.G;
+  const int it0 = int(int64_t(n_it) * split / p.splits);
+  const int it1 = int(int64_t(n_it) * (split + 1) / p.splits);
+  auto head_of = [&](int it) { return kvh * p.G + it / n_qt; };
+  auto qs_of = [&](int it) { return (qt0 + it % n_qt) * BT; };
 
   QTile<Tr, D> tile;
-  tile.load(p, kvh * p.G, qt0 * BT, tid);
-  tile.store(smem, tid);
+  if (it0 < it1) {
+    tile.load(p, head_of(it0), qs_of(it0), tid);
+    tile.store(smem, tid);
+  }
   __syncthreads();
-  if (n_it > 1) tile.load(p, kvh * p.G + 1 % p.G, (qt0 + 1 / p.G) * BT, tid);
+  if (it0 + 1 < it1) tile.load(p, head_of(it0 + 1), qs_of(it0 + 1), tid);
 
-  for (int it = 0; it < n_it; ++it) {
-    const int qs = (qt0 + it / p.G) * BT;
-    const char* st = smem + (it & 1) * C::STAGE;
+  for (int it = it0; it < it1; ++it) {
+    const int qs = qs_of(it);
+    const char* st = smem + ((it - it0) & 1) * C::STAGE;
     const char* qr = st;
     const char* dr = st + C::X_BYTES;
     const char* qt = st + 2 * C::X_BYTES;
@@ -356,17 +394,31 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
       }
     }
 
-    if (it + 1 < n_it) {
-      tile.store(smem + ((it + 1) & 1) * C::STAGE, tid);
-      if (it + 2 < n_it) {
-        const int nx = it + 2;
-        tile.load(p, kvh * p.G + nx % p.G, (qt0 + nx / p.G) * BT, tid);
-      }
+    if (it + 1 < it1) {
+      tile.store(smem + ((it + 1 - it0) & 1) * C::STAGE, tid);
+      if (it + 2 < it1) tile.load(p, head_of(it + 2), qs_of(it + 2), tid);
     }
     __syncthreads();
   }
 
   // Epilogue: lane (key, half) holds d = 32 db + acc_row(r, half).
+  if (p.splits > 1) {
+    // fp32 partial sums, reduced in split order by dkdv_reduce_kernel
+    if (active && key < p.N) {
+      const int64_t off = ((int64_t(split) * p.N + key) * p.hk + kvh) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * half;
+          *reinterpret_cast<f32x4_t*>(p.part_dk + off + d) =
+              f32x4_t{dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2], dkt[db][4 * r4 + 3]};
+          *reinterpret_cast<f32x4_t*>(p.part_dv + off + d) =
+              f32x4_t{dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]};
+        }
+    }
+    return;
+  }
   if (active && key < p.N) {
     constexpr int OE = kF32Out ? 4 : 2;
     const int64_t off = (int64_t(key) * p.hk + kvh) * D * OE;
@@ -385,6 +437,31 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
         store4<kF32Out>(p.dv + off + d * OE, vx);
       }
   }
+}
+
+// Sum of the split partials, in split order (deterministic), then the scale
+// for dK and the output type. One thread per 4 consecutive elements.
+template <bool kF32Out>
+__global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int D) {
+  const int64_t n4 = int64_t(p.N) * p.hk * D / 4;
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t stride = int64_t(p.N) * p.hk * D;
+  float k[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.splits; ++s) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.part_dk + s * stride + 4 * i);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p.part_dv + s * stride + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      k[j] += a[j];
+      v[j] += b[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k[j] *= p.scale;
+  constexpr int OE = kF32Out ? 4 : 2;
+  store4<kF32Out>(p.dk + 4 * i * OE, k);
+  store4<kF32Out>(p.dv + 4 * i * OE, v);
 }
 
 // ----------------------------------------------------------------------------
@@ -611,7 +688,11 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   p.dq = static_cast<char*>(dq);
   p.dk = static_cast<char*>(dk);
   p.dv = static_cast<char*>(dv);
-  p.delta = static_cast<float*>(workspace);
+  const WsLayout wl = ws_layout(d);
+  p.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.delta);
+  p.splits = dkdv_splits(d);
+  p.part_dk = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part);
+  p.part_dv = p.part_dk + (p.splits > 1 ? size_t(p.splits) * d.N * d.hk * d.D : 0);
   p.cu = d.cu;
   p.ndocs = d.ndocs;
   p.N = static_cast<int>(d.N);
@@ -629,10 +710,17 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  p.n_tiles = static_cast<int>((d.N + 32 * kWaves - 1) / (32 * kWaves));
-  dkdv_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles, d.hk), kThreads, 0, stream>>>(p);
+  p.n_tiles = static_cast<int>((d.N + kKeysPerWg - 1) / kKeysPerWg);
+  dkdv_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles * p.splits, d.hk), kThreads, 0, stream>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.splits > 1) {
+    const int64_t n4 = d.N * d.hk * D / 4;
+    dkdv_reduce_kernel<kF32Out><<<dim3(static_cast<unsigned>((n4 + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(
+        p, D);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   const int rows_per_wg = 32 * (kWaves / p.Gw);
   p.n_tiles = static_cast<int>((d.N + rows_per_wg - 1) / rows_per_wg);
@@ -642,10 +730,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
 
 }  // namespace
 
-size_t bwd_workspace_bytes(const AttnDesc& d) {
-  const size_t delta = size_t(4) * size_t(d.hq) * size_t(d.N);
-  return (delta + 255) & ~size_t(255);
-}
+size_t bwd_workspace_bytes(const AttnDesc& d) { return ws_layout(d).total; }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, void* dq, void* dk, void* dv, void* workspace, const AttnDesc& d,

@@ -12,6 +12,7 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
