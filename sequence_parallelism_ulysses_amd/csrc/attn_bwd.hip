@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int kvh = blockIdx.y;
   const int split = int(blockIdx.x) % p.splits;
   const int kv0 = (int(blockIdx.x) / p.splits) * (32 * kWaves);  // first tiles carry the most causal work
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int groups = p.G / p.Gw;
   const int kvh = blockIdx.y / groups, sub = blockIdx.y % groups;
   const int QW = kWaves / p.Gw;

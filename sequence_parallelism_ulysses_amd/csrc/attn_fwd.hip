@@ -35,8 +35,6 @@
 namespace uly {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr int BN = 64;  // keys per tile
 
 struct FwdParams {
@@ -52,10 +50,17 @@ struct FwdParams {
   float scale_log2;
 };
 
+// bf16: 8 waves of 32 query rows (two waves per SIMD, <= 256 registers each,
+// so one wave's softmax overlaps the other's MFMAs). fp32: 4 waves.
+template <class Tr>
+constexpr int waves_for() { return Tr::kElem == 2 ? 8 : 4; }
+
 template <class Tr, int D>
 struct FwdCfg {
+  static constexpr int kWaves = waves_for<Tr>();
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int E = Tr::kElem;
-  static constexpr int QB = (sizeof(typename Tr::frag_t) == 16) ? 2 : 1;  // 32-row blocks per wave
+  static constexpr int QB = 1;  // 32-row blocks per wave
   static constexpr int RW = 32 * QB;
   static constexpr int KS = D / Tr::kStep;  // MFMA steps over D
   static constexpr int DB = D / 32;         // 32-wide blocks of D
@@ -67,7 +72,7 @@ struct FwdCfg {
   static constexpr int V_BYTES = kVt ? D * V_STRIDE : BN * V_STRIDE;
   static constexpr int CPR = D * E / 16;              // 16-byte chunks per row
   static constexpr int K_CH = BN * CPR / kThreads;    // chunks per thread
-  static constexpr int V_PAIRS = (BN / 4) * (D / 8);  // bf16: (4-key group, 8-dim chunk)
+  static constexpr int V_PAIRS = (BN / 4) * (D / 4);  // bf16: (4-key group, 4-dim chunk)
   static constexpr int V_REGS = kVt ? 4 : K_CH;
   static_assert(BN * CPR % kThreads == 0, "tile must split evenly");
   static_assert(!kVt || V_PAIRS <= kThreads, "one V pair per thread at most");
@@ -85,8 +90,9 @@ __device__ __forceinline__ int vt_slot(int kg) {
 template <class Tr, int D>
 struct Tile {
   using C = FwdCfg<Tr, D>;
+  static constexpr int kThreads = C::kThreads;
   u32x4_t k[C::K_CH];
-  u32x4_t v[C::V_REGS];
+  u32x4_t v[C::kVt ? 2 : C::K_CH];  // bf16: four 8-byte rows packed into two 16-byte registers
 
   __device__ __forceinline__ void load(const FwdParams& p, int kvh, int kv0, int tid) {
     const int64_t row_bytes = int64_t(p.hk) * D * C::E;
@@ -103,12 +109,16 @@ struct Tile {
     }
     if constexpr (C::kVt) {
       if (tid < C::V_PAIRS) {
+        // keys 4kg..4kg+3, dims 4dc..4dc+3 (8 bytes per key)
         const int kg = tid % (BN / 4), dc = tid / (BN / 4);
+        u32x2_t r[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kv0 + 4 * kg + i;
-          v[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(vb + key * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
+          r[i] = key < p.N ? *reinterpret_cast<const u32x2_t*>(vb + key * row_bytes + dc * 8) : u32x2_t{0, 0};
         }
+        v[0] = u32x4_t{r[0][0], r[0][1], r[1][0], r[1][1]};
+        v[1] = u32x4_t{r[2][0], r[2][1], r[3][0], r[3][1]};
       }
     }
   }
@@ -123,16 +133,16 @@ struct Tile {
     }
     if constexpr (C::kVt) {
       if (tid < C::V_PAIRS) {
-        // v[i] = key (4kg+i), dims dc*8 .. dc*8+7; word j holds dims 2j (low) and 2j+1 (high).
+        // key i of the group: words (v[i/2][2(i%2)], v[i/2][2(i%2)+1]) hold dims (0,1) and (2,3).
         const int kg = tid % (BN / 4), dc = tid / (BN / 4);
         char* base = lv + vt_slot(kg) * C::E;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w0 = v[0][j], w1 = v[1][j], w2 = v[2][j], w3 = v[3][j];
-          u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-          u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-          *reinterpret_cast<u32x2_t*>(base + (dc * 8 + 2 * j) * C::V_STRIDE) = lo;
-          *reinterpret_cast<u32x2_t*>(base + (dc * 8 + 2 * j + 1) * C::V_STRIDE) = hi;
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t w0 = v[0][j], w1 = v[0][2 + j], w2 = v[1][j], w3 = v[1][2 + j];
+          const u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+          const u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
+          *reinterpret_cast<u32x2_t*>(base + (dc * 4 + 2 * j) * C::V_STRIDE) = lo;
+          *reinterpret_cast<u32x2_t*>(base + (dc * 4 + 2 * j + 1) * C::V_STRIDE) = hi;
         }
       }
     }
@@ -140,14 +150,16 @@ struct Tile {
 };
 
 template <class Tr, int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(FwdCfg<Tr, D>::kThreads, FwdCfg<Tr, D>::kThreads),
+                          amdgpu_waves_per_eu(FwdCfg<Tr, D>::kWaves / 4, FwdCfg<Tr, D>::kWaves / 4)))
+void attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<Tr, D>;
   using frag_t = typename Tr::frag_t;
-  constexpr int E = C::E, QB = C::QB, RW = C::RW;
+  constexpr int E = C::E, QB = C::QB, RW = C::RW, kWaves = C::kWaves;
   __shared__ __attribute__((aligned(16))) char smem[2 * (C::K_BYTES + C::V_BYTES)];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int groups = p.G / p.Gw;
   const int kvh = blockIdx.y / groups, sub = blockIdx.y % groups;
   const int QW = kWaves / p.Gw;
@@ -205,6 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
     const char* lv = lk + C::K_BYTES;
 
     if (active && kv0 <= wq_last && kv0 + BN > w_ds_first) {
+      // element-wise mask only on the diagonal tile and tiles crossing a document start
+      const bool need_mask = __builtin_expect(kv0 + BN - 1 > qbase || kv0 < w_ds_last, 0);
       // S^T tile: keys (2 blocks of 32) x this wave's query columns.
       f32x16_t s[2][QB];
 #pragma unroll
@@ -221,7 +235,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
         }
       }
 
-      const bool need_mask = (kv0 + BN - 1 > qbase) || (kv0 < w_ds_last);
       frag_t pf[QB][C::PV];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -239,14 +252,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][qb][r]);
-        mt = xhalf_max(mt);
-        const float m_new = fmaxf(m[qb], mt * p.scale_log2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m[qb] - m_use);
-        m[qb] = m_new;
-        l[qb] *= alpha;
+        mt = xhalf_max(mt) * p.scale_log2;
+        // raise the running max only when the tile's max exceeds it by > 2^8
+        const bool grow = mt > m[qb] + kRescaleLog2;
+        if (wave_any(grow)) {
+          // lanes that do not grow keep their max (alpha 1, also when it is still -inf);
+          // a growing lane whose max was -inf gets alpha 0
+          const float alpha = grow ? fast_exp2(m[qb] - mt) : 1.f;
+          m[qb] = grow ? mt : m[qb];
+          l[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc_o[db][qb] *= alpha;
+          for (int db = 0; db < C::DB; ++db) acc_o[db][qb] *= alpha;
+        }
+        const float m_use = m[qb] == -INFINITY ? 0.f : m[qb];
         float pv[32];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -328,12 +346,12 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   p.hq = d.hq;
   p.hk = d.hk;
   p.G = d.hq / d.hk;
-  p.Gw = std::gcd(p.G, kWaves);
-  const int rows = C::RW * (kWaves / p.Gw);
+  p.Gw = std::gcd(p.G, C::kWaves);
+  const int rows = C::RW * (C::kWaves / p.Gw);
   p.n_qtiles = static_cast<int>((d.N + rows - 1) / rows);
   p.scale_log2 = d.scale * kLog2e;
   dim3 grid(p.n_qtiles, d.hk * (p.G / p.Gw));
-  attn_fwd_kernel<Tr, D><<<grid, kThreads, 0, stream>>>(p);
+  attn_fwd_kernel<Tr, D><<<grid, C::kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
