@@ -31,6 +31,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_tile.hpp"
 
 namespace uly {
 namespace {
@@ -330,6 +331,185 @@ void attn_fwd_kernel(FwdParams p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 kernel: K and V tiles stay row-major in LDS (swizzled, see
+// lds_tile.hpp), filled by asynchronous buffer loads into a three-stage ring
+// (tile t+2 in flight while tile t is consumed, one barrier per tile); V^T
+// operands come from ds_read_b64_tr_b16. No register staging, no transposing
+// stores.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FwdBf {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int KS = D / 16;  // MFMA steps over D
+  static constexpr int DB = D / 32;  // 32-wide blocks of D
+  static constexpr int TB = TileFmt<D>::kBytes;
+  static constexpr int STAGE = 2 * TB;  // K tile, V tile
+  static constexpr int NSTAGE = 3;
+  static constexpr int LOADS = 2 * tile_loads<D, kThreads>();  // per thread per stage
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_kernel(FwdParams p) {
+  using C = FwdBf<D>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::NSTAGE * C::STAGE];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int groups = p.G / p.Gw;
+  const int kvh = blockIdx.y / groups, sub = blockIdx.y % groups;
+  const int QW = C::kWaves / p.Gw;
+  const int qtile = p.n_qtiles - 1 - int(blockIdx.x);  // heaviest first
+  const int wg_q0 = qtile * 32 * QW;
+  const int wg_q1 = min(p.N, wg_q0 + 32 * QW);
+  const int head = kvh * p.G + sub * p.Gw + (w % p.Gw);
+  const int qbase = wg_q0 + (w / p.Gw) * 32;
+  const bool active = qbase < p.N;
+  const int wq_last = min(qbase + 31, p.N - 1);
+  const int my_q = qbase + l32;
+  const int my_ds = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1)).start;
+  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
+  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+
+  // Q fragments (B operand of S^T = K Q^T), zero past N.
+  bf16x8_t qf[C::KS];
+  const int64_t q_row = int64_t(p.hq) * D * 2;
+  {
+    const char* src = p.q + int64_t(my_q) * q_row + int64_t(head) * D * 2 + half * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qf[ks] = my_q < p.N ? *reinterpret_cast<const bf16x8_t*>(src + ks * 32) : bf16x8_t{};
+  }
+
+  f32x16_t acc_o[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc_o[db] = f32x16_t{};
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
+  const int t0 = kv_begin / BN, t1 = (wg_q1 - 1) / BN;
+  const uint32_t kv_row = uint32_t(p.hk) * D * 2;
+
+  auto issue = [&](int t) {
+    lds_char* st = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
+    const int kv0 = t * BN;
+    const uint32_t bytes = uint32_t(min(BN, p.N - kv0)) * kv_row;
+    const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
+    issue_tile<D, C::kThreads>(make_rsrc(p.k + off, bytes), kv_row, st, tid);
+    issue_tile<D, C::kThreads>(make_rsrc(p.v + off, bytes), kv_row, st + C::TB, tid);
+  };
+  issue(t0);
+  if (t0 + 1 <= t1) issue(t0 + 1);
+
+  for (int t = t0; t <= t1; ++t) {
+    if (t + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();  // this thread's copies of tile t landed
+    __syncthreads();                                                 // everyone's landed; stage t-1 is free
+    const int kv0 = t * BN;
+    const lds_char* lk = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
+    const lds_char* lv = lk + C::TB;
+
+    if (active && kv0 <= wq_last && kv0 + BN > w_ds_first) {
+      // element-wise mask only on the diagonal tile and tiles crossing a document start
+      const bool need_mask = kv0 + BN - 1 > qbase || kv0 < w_ds_last;
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(frag_rows<D>(lk, kb * 32 + l32, ks * 16, half), qf[ks], s[kb]);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kb * 32 + acc_row(r, half);
+            if (key > my_q || key < my_ds) s[kb][r] = -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      mt = xhalf_max(mt) * p.scale_log2;
+      // raise the running max only when the tile's max exceeds it by > 2^8
+      const bool grow = mt > m + kRescaleLog2;
+      if (wave_any(grow)) {
+        const float alpha = grow ? fast_exp2(m - mt) : 1.f;  // 0 when m was -inf
+        m = grow ? mt : m;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc_o[db] *= alpha;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
+      float pv[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -m_use));
+          pv[kb * 16 + r] = e;
+          l += e;
+        }
+      // O^T += V^T P^T, 16 keys per step; V^T read transposed from the row-major tile
+#pragma unroll
+      for (int st = 0; st < BN / 16; ++st) {
+        const bf16x8_t pf = make_frag<TrBF16>(&pv[st * 8]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc_o[db] = mfma(frag_cols_tr<D>(lv, st * 16, db * 32, lane), pf, acc_o[db]);
+      }
+    }
+    // Refill the stage every wave finished with (tile t-1) only now: the
+    // compiler waits for all in-flight LDS copies before transposed LDS
+    // reads, so a copy issued before this tile's reads would stall them.
+    if (t + 2 <= t1) issue(t + 2);
+  }
+
+  const float lsum = xhalf_sum(l);
+  if (active && my_q < p.N) {
+    const float inv = 1.f / lsum;
+    char* dst = p.o + int64_t(my_q) * q_row + int64_t(head) * D * 2;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + 8 * r4 + 4 * half;
+        *reinterpret_cast<u32x2_t*>(dst + d * 2) =
+            u32x2_t{pack_bf16x2(acc_o[db][4 * r4] * inv, acc_o[db][4 * r4 + 1] * inv),
+                    pack_bf16x2(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv)};
+      }
+    if (half == 0) p.lse[int64_t(head) * p.N + my_q] = (m + log2f(lsum)) * kLn2;
+  }
+}
+
+template <int D>
+hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnDesc& d,
+                       hipStream_t stream) {
+  using C = FwdBf<D>;
+  FwdParams p;
+  p.q = static_cast<const char*>(q);
+  p.k = static_cast<const char*>(k);
+  p.v = static_cast<const char*>(v);
+  p.o = static_cast<char*>(o);
+  p.lse = lse;
+  p.cu = d.cu;
+  p.ndocs = d.ndocs;
+  p.N = static_cast<int>(d.N);
+  p.hq = d.hq;
+  p.hk = d.hk;
+  p.G = d.hq / d.hk;
+  p.Gw = std::gcd(p.G, C::kWaves);
+  const int rows = 32 * (C::kWaves / p.Gw);
+  p.n_qtiles = static_cast<int>((d.N + rows - 1) / rows);
+  p.scale_log2 = d.scale * kLog2e;
+  dim3 grid(p.n_qtiles, d.hk * (p.G / p.Gw));
+  attn_fwd_bf16_kernel<D><<<grid, C::kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <class Tr, int D>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, const AttnDesc& d,
                   hipStream_t stream) {
@@ -360,8 +540,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const AttnDesc& d, hipStream_t stream) {
   if (d.dt == ULY_BF16)
-    return d.D == 128 ? launch<TrBF16, 128>(q, k, v, o, lse, d, stream)
-                      : launch<TrBF16, 64>(q, k, v, o, lse, d, stream);
+    return d.D == 128 ? launch_bf16<128>(q, k, v, o, lse, d, stream) : launch_bf16<64>(q, k, v, o, lse, d, stream);
   return d.D == 128 ? launch<TrF32, 128>(q, k, v, o, lse, d, stream)
                     : launch<TrF32, 64>(q, k, v, o, lse, d, stream);
 }

@@ -1,0 +1,120 @@
+// LDS tiles for the bf16 attention kernels (gfx950).
+//
+// A tile holds 64 consecutive token rows of one head of a [N][H][D] bf16
+// tensor, row-major in LDS (2*D bytes per row, no padding). The 16-byte chunk
+// index inside a row is XOR-swizzled by a function of the row so that both
+// ways the kernels read a tile are bank-conflict free:
+//   - ds_read_b128 of an MFMA operand: 16 consecutive rows, same chunk;
+//   - ds_read_b64_tr_b16 of a transposed operand: 4 consecutive rows x one
+//     aligned 64-byte block per half-wave.
+// Tiles are filled by buffer_load ... lds (16 bytes per lane, written to
+// consecutive LDS addresses), so each lane fetches the global chunk that the
+// swizzle places at its LDS slot; rows past the end of the tensor are outside
+// the buffer resource's range and read as zero.
+#pragma once
+
+#include "common.hpp"
+
+namespace uly {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int D>
+struct TileFmt {
+  static constexpr int kRows = 64;
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  static constexpr int kBytes = kRows * kRowBytes;
+  static_assert(D == 64 || D == 128, "head dim");
+
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (D == 128) {
+      // rows 0..15 -> a permutation of 0..15 whose bits 2-3 differ for any 4 consecutive rows
+      return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+      // 128-byte rows alternate bank halves; rows of equal parity get distinct chunks
+      const int x = row >> 1;
+      return ((x & 1) << 2) | ((x >> 1) & 3);
+    }
+  }
+  // byte offset of logical chunk `chunk` of `row`
+  __device__ static __forceinline__ int off(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+  }
+};
+
+// Buffer resource over `bytes` bytes from `base`: loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Issue the asynchronous copy of one tile: rows [0, 64) of a tensor whose
+// row r, head slice starts at byte r*row_stride from the resource base
+// (rows past the resource's range read as zero). NT threads each issue
+// 64*D*2/16/NT loads of 16 bytes; returns nothing, completion is counted by
+// vmcnt in issue order.
+template <int D, int NT>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t row_stride, lds_char* tile, int tid) {
+  using F = TileFmt<D>;
+  constexpr int kLoads = F::kRows * F::kChunks / NT;
+  static_assert(F::kRows * F::kChunks % NT == 0, "tile split");
+  const int lane = tid & 63, wave_base = tid & ~63;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int slot = NT * i + tid;               // 16-byte slot in the tile, consecutive per lane
+    const int row = slot / F::kChunks;
+    const int chunk = (slot % F::kChunks) ^ F::swz(row);  // logical chunk stored at this slot
+    lds_char* dst = tile + 16 * (NT * i + wave_base);     // wave-uniform base; lane adds 16*lane
+    (void)lane;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                             row * row_stride + chunk * 16, 0, 0, 0);
+  }
+}
+
+template <int D, int NT>
+constexpr int tile_loads() { return 64 * (D / 8) / NT; }
+
+// Wait until at most `n` vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; exp/lgkm counters
+// left at their maximum, i.e. not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// MFMA operand fragment (8 bf16 k-values per lane) for a 32-row block of a
+// row-major tile: lane (row = r0 + l%32, half h) reads k = k0 + 8h .. +7,
+// which are contiguous columns -> one ds_read_b128.
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_rows(const lds_char* tile, int row, int k0, int half) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+      tile + TileFmt<D>::off(row, (k0 >> 3) + half));
+}
+
+// Transposed MFMA operand (32x32x16 A operand over the tile's rows): lane
+// (m = col0 + l%32, half h) needs tile[k][m] for the 8 tile rows
+// k = k0 + {4h..4h+3, 8+4h..8+4h+3}, i.e. the same k order as a fragment
+// built from a 32x32 accumulator (rows 8*(r/4) + 4h + r%4). Two
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i%4 of the 8-byte piece read by lane 4j + i/4 (j = 0..3), so lane 4j + q
+// of group g points at row k0 + 4h + j (+8) and columns
+// col0 + 16*(g%2) + 4q .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_cols_tr(const lds_char* tile, int k0, int col0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int j = i >> 2, q = i & 3, h = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * q;  // multiple of 4 -> half of a 16-byte chunk
+  const int r0 = k0 + 4 * h + j;
+  const int b0 = TileFmt<D>::off(r0, col >> 3) + ((col & 4) << 1);
+  const int b1 = TileFmt<D>::off(r0 + 8, col >> 3) + ((col & 4) << 1);
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + b0));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + b1));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+}  // namespace uly
