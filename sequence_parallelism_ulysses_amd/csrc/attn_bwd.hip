@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_tile.hpp"
 
 namespace uly {
 namespace {
@@ -51,6 +52,7 @@ struct BwdParams {
   char* dk;
   char* dv;
   float* delta;
+  float* lse2;     // lse * log2(e), [hq][N]
   float* part_dk;  // [splits][N][hk][D] fp32, when splits > 1
   float* part_dv;
   const int32_t* cu;
@@ -73,16 +75,17 @@ int dkdv_splits(const AttnDesc& d) {
 }
 
 struct WsLayout {
-  size_t delta, part, total;
+  size_t delta, lse2, part, total;
 };
 WsLayout ws_layout(const AttnDesc& d) {
   WsLayout w;
+  const size_t row_bytes = (size_t(4) * d.hq * d.N + 255) & ~size_t(255);
   w.delta = 0;
-  const size_t delta_bytes = (size_t(4) * d.hq * d.N + 255) & ~size_t(255);
-  w.part = delta_bytes;
+  w.lse2 = row_bytes;
+  w.part = 2 * row_bytes;
   const int s = dkdv_splits(d);
   const size_t part_bytes = s > 1 ? size_t(2) * s * d.N * d.hk * d.D * 4 : 0;
-  w.total = delta_bytes + part_bytes;
+  w.total = w.part + part_bytes;
   return w;
 }
 
@@ -168,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdParams p) {
   if (row < rows && sub == 0) {
     const int64_t q = row / p.hq, h = row % p.hq;
     p.delta[h * p.N + q] = acc;
+    p.lse2[h * p.N + q] = p.lse[h * p.N + q] * kLog2e;
   }
 }
 
@@ -675,6 +679,305 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
   }
 }
 
+
+// ----------------------------------------------------------------------------
+// bf16 kernels on row-major LDS tiles (lds_tile.hpp): every tile is copied by
+// buffer_load ... lds into a three-stage ring, and the transposed operands
+// (Q^T, dO^T, K^T) are read with ds_read_b64_tr_b16 instead of being stored
+// twice. One barrier per tile; a stage is refilled only after the tile's LDS
+// reads (the compiler waits for in-flight LDS copies before transposed reads).
+// ----------------------------------------------------------------------------
+template <int D>
+struct KvBf {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int TB = TileFmt<D>::kBytes;
+  static constexpr int STAGE = 2 * TB + 2 * 64 * 4;  // Q, dO, lse2[64], delta[64]
+  static constexpr int NSTAGE = 3;
+  static constexpr int LOADS = 2 * tile_loads<D, kThreads>() + 2;
+};
+
+template <int D, bool kF32Out>
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
+  using C = KvBf<D>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::NSTAGE * C::STAGE];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int kvh = blockIdx.y;
+  const int split = int(blockIdx.x) % p.splits;
+  const int kv0 = (int(blockIdx.x) / p.splits) * (32 * C::kWaves);  // first tiles carry the most causal work
+  const int kw0 = kv0 + 32 * w;
+  const bool active = kw0 < p.N;
+  const int key = kw0 + l32;
+  const int my_de = doc_of(p.cu, p.ndocs, p.N, min(key, p.N - 1)).end;
+  const int w_de_first = doc_of(p.cu, p.ndocs, p.N, min(kw0, p.N - 1)).end;
+  const int w_de_last = doc_of(p.cu, p.ndocs, p.N, min(kw0 + 31, p.N - 1)).end;
+
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
+  bf16x8_t kf[C::KS], vf[C::KS];
+  {
+    const int64_t off = (int64_t(key) * p.hk + kvh) * D * 2 + half * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = key < p.N ? *reinterpret_cast<const bf16x8_t*>(p.k + off + ks * 32) : bf16x8_t{};
+      vf[ks] = key < p.N ? *reinterpret_cast<const bf16x8_t*>(p.v + off + ks * 32) : bf16x8_t{};
+    }
+  }
+  f32x16_t dkt[C::DB], dvt[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dkt[db] = dvt[db] = f32x16_t{};
+
+  // Queries that can see any of the 128 keys: [kv0, end of the last key's
+  // document). The (q head, query tile) iterations over them, head-major, are
+  // split evenly between p.splits workgroups; this one takes [it0, it1).
+  const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + 32 * C::kWaves - 1, p.N - 1)).end;
+  const int qt0 = kv0 / BT;
+  const int n_qt = (q_end - 1) / BT - qt0 + 1;
+  const int n_it = n_qt * p.G;
+  const int it0 = int(int64_t(n_it) * split / p.splits);
+  const int it1 = int(int64_t(n_it) * (split + 1) / p.splits);
+  const uint32_t q_row = uint32_t(p.hq) * D * 2;
+
+  auto issue = [&](int it) {
+    lds_char* st = smem + ((it - it0) % C::NSTAGE) * C::STAGE;
+    const int head = kvh * p.G + it / n_qt;
+    const int qs = (qt0 + it % n_qt) * BT;
+    const int rows = min(BT, p.N - qs);
+    const int64_t off = (int64_t(qs) * p.hq + head) * D * 2;
+    issue_tile<D, C::kThreads>(make_rsrc(p.q + off, uint32_t(rows) * q_row), q_row, st, tid);
+    issue_tile<D, C::kThreads>(make_rsrc(p.dout + off, uint32_t(rows) * q_row), q_row, st + C::TB, tid);
+    // 64 floats of lse2 and delta (every wave copies the same values)
+    const int64_t foff = int64_t(head) * p.N + qs;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.lse2 + foff, uint32_t(rows) * 4),
+                                             (__attribute__((address_space(3))) void*)(st + 2 * C::TB), 4, lane * 4, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.delta + foff, uint32_t(rows) * 4),
+                                             (__attribute__((address_space(3))) void*)(st + 2 * C::TB + 256), 4, lane * 4,
+                                             0, 0, 0);
+  };
+  if (it0 < it1) issue(it0);
+  if (it0 + 1 < it1) issue(it0 + 1);
+
+  for (int it = it0; it < it1; ++it) {
+    if (it + 1 < it1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
+    __syncthreads();
+    const int qs = (qt0 + it % n_qt) * BT;
+    const lds_char* qt = smem + ((it - it0) % C::NSTAGE) * C::STAGE;
+    const lds_char* dt = qt + C::TB;
+    typedef __attribute__((address_space(3))) const float lds_float;
+    lds_float* fl = (lds_float*)(qt + 2 * C::TB);
+
+    if (active && qs + BT - 1 >= kw0 && qs < w_de_last) {
+      const bool need_mask = (qs < kw0 + 31) || (qs + BT > w_de_first);
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = mfma(frag_rows<D>(qt, qb * 32 + l32, ks * 16, half), kf[ks], s[qb]);
+          dp[qb] = mfma(frag_rows<D>(dt, qb * 32 + l32, ks * 16, half), vf[ks], dp[qb]);
+        }
+      float pv[32], dsv[32];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi = qb * 32 + 8 * r4 + 4 * half;  // first of 4 consecutive queries
+          typedef __attribute__((address_space(3))) const f32x4_t lds_f32x4;
+          const f32x4_t l4 = *(lds_f32x4*)(fl + qi);
+          const f32x4_t d4 = *(lds_f32x4*)(fl + 64 + qi);
+          const float lv[4] = {l4[0], l4[1], l4[2], l4[3]};
+          const float dv4[4] = {d4[0], d4[1], d4[2], d4[3]};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * r4 + j;
+            float e = fast_exp2(fmaf(s[qb][r], p.scale_log2, -lv[j]));
+            if (need_mask) {
+              const int q = qs + qi + j;
+              if (q < key || q >= my_de) e = 0.f;
+            }
+            pv[qb * 16 + r] = e;
+            dsv[qb * 16 + r] = e * (dp[qb][r] - dv4[j]);
+          }
+        }
+      // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the tile's 64 queries)
+#pragma unroll
+      for (int st2 = 0; st2 < BT / 16; ++st2) {
+        const bf16x8_t pf = make_frag<TrBF16>(&pv[st2 * 8]);
+        const bf16x8_t sf = make_frag<TrBF16>(&dsv[st2 * 8]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          dvt[db] = mfma(frag_cols_tr<D>(dt, st2 * 16, db * 32, lane), pf, dvt[db]);
+          dkt[db] = mfma(frag_cols_tr<D>(qt, st2 * 16, db * 32, lane), sf, dkt[db]);
+        }
+      }
+    }
+    if (it + 2 < it1) issue(it + 2);
+  }
+
+  if (p.splits > 1) {
+    // fp32 partial sums, reduced in split order by dkdv_reduce_kernel
+    if (active && key < p.N) {
+      const int64_t off = ((int64_t(split) * p.N + key) * p.hk + kvh) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * half;
+          *reinterpret_cast<f32x4_t*>(p.part_dk + off + d) =
+              f32x4_t{dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2], dkt[db][4 * r4 + 3]};
+          *reinterpret_cast<f32x4_t*>(p.part_dv + off + d) =
+              f32x4_t{dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]};
+        }
+    }
+    return;
+  }
+  if (active && key < p.N) {
+    constexpr int OE = kF32Out ? 4 : 2;
+    const int64_t off = (int64_t(key) * p.hk + kvh) * D * OE;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + 8 * r4 + 4 * half;
+        float kx[4], vx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[j] = dkt[db][4 * r4 + j] * p.scale;
+          vx[j] = dvt[db][4 * r4 + j];
+        }
+        store4<kF32Out>(p.dk + off + d * OE, kx);
+        store4<kF32Out>(p.dv + off + d * OE, vx);
+      }
+  }
+}
+
+template <int D>
+struct DqBf {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int TB = TileFmt<D>::kBytes;
+  static constexpr int STAGE = 2 * TB;  // K, V
+  static constexpr int NSTAGE = 3;
+  static constexpr int LOADS = 2 * tile_loads<D, kThreads>();
+};
+
+template <int D, bool kF32Out>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void dq_bf16_kernel(BwdParams p) {
+  using C = DqBf<D>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::NSTAGE * C::STAGE];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int groups = p.G / p.Gw;
+  const int kvh = blockIdx.y / groups, sub = blockIdx.y % groups;
+  const int QW = C::kWaves / p.Gw;
+  const int qtile = p.n_tiles - 1 - int(blockIdx.x);  // heaviest first
+  const int wg_q0 = qtile * 32 * QW;
+  const int wg_q1 = min(p.N, wg_q0 + 32 * QW);
+  const int head = kvh * p.G + sub * p.Gw + (w % p.Gw);
+  const int qbase = wg_q0 + (w / p.Gw) * 32;
+  const bool active = qbase < p.N;
+  const int wq_last = min(qbase + 31, p.N - 1);
+  const int my_q = qbase + l32;
+  const bool q_ok = my_q < p.N;
+  const int my_ds = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1)).start;
+  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
+  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+  const float my_lse2 = q_ok ? p.lse2[int64_t(head) * p.N + my_q] : 0.f;
+  const float my_dlt = q_ok ? p.delta[int64_t(head) * p.N + my_q] : 0.f;
+
+  bf16x8_t qf[C::KS], df[C::KS];
+  {
+    const int64_t off = (int64_t(my_q) * p.hq + head) * D * 2 + half * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      qf[ks] = q_ok ? *reinterpret_cast<const bf16x8_t*>(p.q + off + ks * 32) : bf16x8_t{};
+      df[ks] = q_ok ? *reinterpret_cast<const bf16x8_t*>(p.dout + off + ks * 32) : bf16x8_t{};
+    }
+  }
+  f32x16_t dqt[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dqt[db] = f32x16_t{};
+
+  const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
+  const int t0 = kv_begin / BT, t1 = (wg_q1 - 1) / BT;
+  const uint32_t kv_row = uint32_t(p.hk) * D * 2;
+
+  auto issue = [&](int t) {
+    lds_char* st = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
+    const int kv0 = t * BT;
+    const uint32_t bytes = uint32_t(min(BT, p.N - kv0)) * kv_row;
+    const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
+    issue_tile<D, C::kThreads>(make_rsrc(p.k + off, bytes), kv_row, st, tid);
+    issue_tile<D, C::kThreads>(make_rsrc(p.v + off, bytes), kv_row, st + C::TB, tid);
+  };
+  issue(t0);
+  if (t0 + 1 <= t1) issue(t0 + 1);
+
+  for (int t = t0; t <= t1; ++t) {
+    if (t + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
+    __syncthreads();
+    const int kv0 = t * BT;
+    const lds_char* kr = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
+    const lds_char* vr = kr + C::TB;
+
+    if (active && kv0 <= wq_last && kv0 + BT > w_ds_first) {
+      const bool need_mask = (kv0 + BT - 1 > qbase) || (kv0 < w_ds_last);
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = mfma(frag_rows<D>(kr, kb * 32 + l32, ks * 16, half), qf[ks], s[kb]);
+          dp[kb] = mfma(frag_rows<D>(vr, kb * 32 + l32, ks * 16, half), df[ks], dp[kb]);
+        }
+      float dsv[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
+          if (need_mask) {
+            const int k = kv0 + kb * 32 + acc_row(r, half);
+            if (k > my_q || k < my_ds) e = 0.f;
+          }
+          dsv[kb * 16 + r] = e * (dp[kb][r] - my_dlt);
+        }
+      // dQ^T += K^T dS^T, K^T read transposed from the row-major K tile
+#pragma unroll
+      for (int st2 = 0; st2 < BT / 16; ++st2) {
+        const bf16x8_t sf = make_frag<TrBF16>(&dsv[st2 * 8]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) dqt[db] = mfma(frag_cols_tr<D>(kr, st2 * 16, db * 32, lane), sf, dqt[db]);
+      }
+    }
+    if (t + 2 <= t1) issue(t + 2);
+  }
+
+  if (active && q_ok) {
+    constexpr int OE = kF32Out ? 4 : 2;
+    char* dst = p.dq + (int64_t(my_q) * p.hq + head) * D * OE;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + 8 * r4 + 4 * half;
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = dqt[db][4 * r4 + j] * p.scale;
+        store4<kF32Out>(dst + d * OE, x);
+      }
+  }
+}
+
 template <class Tr, int D, bool kF32Out>
 hipError_t launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, void* workspace, const AttnDesc& d, hipStream_t stream) {
@@ -690,6 +993,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   p.dv = static_cast<char*>(dv);
   const WsLayout wl = ws_layout(d);
   p.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.delta);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse2);
   p.splits = dkdv_splits(d);
   p.part_dk = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part);
   p.part_dv = p.part_dk + (p.splits > 1 ? size_t(p.splits) * d.N * d.hk * d.D : 0);
@@ -711,7 +1015,10 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   if (e != hipSuccess) return e;
 
   p.n_tiles = static_cast<int>((d.N + kKeysPerWg - 1) / kKeysPerWg);
-  dkdv_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles * p.splits, d.hk), kThreads, 0, stream>>>(p);
+  if constexpr (Tr::kElem == 2)
+    dkdv_bf16_kernel<D, kF32Out><<<dim3(p.n_tiles * p.splits, d.hk), KvBf<D>::kThreads, 0, stream>>>(p);
+  else
+    dkdv_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles * p.splits, d.hk), kThreads, 0, stream>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
@@ -722,9 +1029,16 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
     if (e != hipSuccess) return e;
   }
 
-  const int rows_per_wg = 32 * (kWaves / p.Gw);
-  p.n_tiles = static_cast<int>((d.N + rows_per_wg - 1) / rows_per_wg);
-  dq_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles, d.hk * (p.G / p.Gw)), kThreads, 0, stream>>>(p);
+  if constexpr (Tr::kElem == 2) {
+    p.Gw = std::gcd(p.G, DqBf<D>::kWaves);
+    const int rows_per_wg = 32 * (DqBf<D>::kWaves / p.Gw);
+    p.n_tiles = static_cast<int>((d.N + rows_per_wg - 1) / rows_per_wg);
+    dq_bf16_kernel<D, kF32Out><<<dim3(p.n_tiles, d.hk * (p.G / p.Gw)), DqBf<D>::kThreads, 0, stream>>>(p);
+  } else {
+    const int rows_per_wg = 32 * (kWaves / p.Gw);
+    p.n_tiles = static_cast<int>((d.N + rows_per_wg - 1) / rows_per_wg);
+    dq_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles, d.hk * (p.G / p.Gw)), kThreads, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
