@@ -35,14 +35,10 @@ def hipcc() -> str:
     return path
 
 
-# Per-file code-generation flags. The key-stationary dK/dV kernel runs one wave
-# per SIMD, so its schedule must hide latency inside the wave: keep MFMA
-# accumulators in VGPRs and schedule for ILP (measured: 535 -> 672 TFLOP/s for
-# the backward at 32k tokens). The two-waves-per-SIMD kernels are faster with
-# the default scheduler.
-FILE_FLAGS = {
-    "attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-}
+# Per-file code-generation flags (file name -> extra hipcc arguments). Every
+# kernel now runs two waves per SIMD and is fastest with the default
+# scheduler, so none are set; the hook stays for kernels that need their own.
+FILE_FLAGS: dict = {}
 
 
 def sources() -> list[str]:

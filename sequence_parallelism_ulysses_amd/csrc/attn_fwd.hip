@@ -347,7 +347,7 @@ struct FwdBf {
   static constexpr int DB = D / 32;  // 32-wide blocks of D
   static constexpr int TB = TileFmt<D>::kBytes;
   static constexpr int STAGE = 2 * TB;  // K tile, V tile
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = 4;
   static constexpr int LOADS = 2 * tile_loads<D, kThreads>();  // per thread per stage
 };
 
@@ -389,6 +389,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc_o[db] = f32x16_t{};
   float m = -INFINITY, l = 0.f;
+  RowFragOffsets<D> ko;
+  TrFragOffsets<D> vo;
+  ko.init(lane);
+  vo.init(lane);
 
   const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
   const int t0 = kv_begin / BN, t1 = (wg_q1 - 1) / BN;
@@ -402,24 +406,47 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     issue_tile<D, C::kThreads>(make_rsrc(p.k + off, bytes), kv_row, st, tid);
     issue_tile<D, C::kThreads>(make_rsrc(p.v + off, bytes), kv_row, st + C::TB, tid);
   };
-  issue(t0);
-  if (t0 + 1 <= t1) issue(t0 + 1);
+  // Software pipeline over key tiles: while the softmax of tile t runs on the
+  // VALU, the MFMAs of S(t+1) = K(t+1) Q^T are already in flight, so each
+  // wave has independent matrix work during its exponentials. K(t+1) must be
+  // resident one tile early; a four-stage ring keeps two tiles of copies in
+  // flight behind it.
+  auto sees = [&](int t) {
+    const int kv0 = t * BN;
+    return active && kv0 <= wq_last && kv0 + BN > w_ds_first;
+  };
+  auto compute_s = [&](int t, f32x16_t (&s)[2]) {
+    const lds_char* lk = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const lds_char* ka = lds_base(lk, ko.off[ks]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(frag_rows_at<D>(ka, kb * 64 * D), qf[ks], s[kb]);
+    }
+  };
+
+  for (int i = 0; i < 3; ++i)
+    if (t0 + i <= t1) issue(t0 + i);
+  if (t0 + 2 <= t1) wait_vmcnt<2 * C::LOADS>(); else if (t0 + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
+  __syncthreads();
+  f32x16_t s_cur[2], s_nxt[2];
+  if (sees(t0)) compute_s(t0, s_cur);
 
   for (int t = t0; t <= t1; ++t) {
-    if (t + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();  // this thread's copies of tile t landed
-    __syncthreads();                                                 // everyone's landed; stage t-1 is free
+    // tile t+1 (its K feeds S(t+1) now) must have landed; t+2 may be in flight
+    if (t + 2 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
+    __syncthreads();  // everyone's copies landed; stage t-1 is free
     const int kv0 = t * BN;
-    const lds_char* lk = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
-    const lds_char* lv = lk + C::TB;
+    const lds_char* lv = smem + ((t - t0) % C::NSTAGE) * C::STAGE + C::TB;
+    const bool next = t + 1 <= t1 && sees(t + 1);
+    if (next) compute_s(t + 1, s_nxt);
 
-    if (active && kv0 <= wq_last && kv0 + BN > w_ds_first) {
+    if (sees(t)) {
+      f32x16_t (&s)[2] = s_cur;
       // element-wise mask only on the diagonal tile and tiles crossing a document start
       const bool need_mask = kv0 + BN - 1 > qbase || kv0 < w_ds_last;
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(frag_rows<D>(lk, kb * 32 + l32, ks * 16, half), qf[ks], s[kb]);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -455,17 +482,28 @@ void attn_fwd_bf16_kernel(FwdParams p) {
           l += e;
         }
       // O^T += V^T P^T, 16 keys per step; V^T read transposed from the row-major tile
+      const lds_char* va[2][C::DB];
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        va[0][db] = lds_base(lv, vo.off[0][db]);
+        va[1][db] = lds_base(lv, vo.off[1][db]);
+      }
 #pragma unroll
       for (int st = 0; st < BN / 16; ++st) {
         const bf16x8_t pf = make_frag<TrBF16>(&pv[st * 8]);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc_o[db] = mfma(frag_cols_tr<D>(lv, st * 16, db * 32, lane), pf, acc_o[db]);
+        for (int db = 0; db < C::DB; ++db)
+          acc_o[db] = mfma(frag_tr2(va[0][db], va[1][db], st * 32 * D), pf, acc_o[db]);
       }
     }
-    // Refill the stage every wave finished with (tile t-1) only now: the
-    // compiler waits for all in-flight LDS copies before transposed LDS
-    // reads, so a copy issued before this tile's reads would stall them.
-    if (t + 2 <= t1) issue(t + 2);
+    if (next) {
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
+    }
+    // Refill the stage every wave finished with (tile t-1) only after this
+    // tile's LDS reads: the compiler waits for all in-flight LDS copies
+    // before transposed LDS reads.
+    if (t + 3 <= t1) issue(t + 3);
   }
 
   const float lsum = xhalf_sum(l);

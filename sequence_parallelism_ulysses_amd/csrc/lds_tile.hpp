@@ -117,4 +117,74 @@ __device__ __forceinline__ bf16x8_t frag_cols_tr(const lds_char* tile, int k0, i
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Per-lane byte offsets of the fragments a wave reads from a tile, computed
+// once outside the main loop so each LDS read in it is (stage base + a
+// precomputed offset + an immediate).
+//
+// Row fragments (frag_rows): rows rb*32 + l%32, k = 16*ks + 8h. The swizzle
+// of row rb*32 + l%32 equals that of l%32, so the offset of (rb, ks) is
+// rows_off[ks] + rb*32*2D.
+template <int D>
+struct RowFragOffsets {
+  int off[D / 16];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) off[ks] = TileFmt<D>::off(l32, 2 * ks + half);
+  }
+};
+
+// Transposed fragments (frag_cols_tr) over tile rows k0 = 16*st (+0 / +8)
+// and output columns col0 = 32*db: the swizzle of those rows does not depend
+// on st, so the offset of (st, part, db) is off[part][db] + st*16*2D.
+template <int D>
+struct TrFragOffsets {
+  int off[2][D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int j = i >> 2, q = i & 3, h = g >> 1;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int col = 32 * db + 16 * (g & 1) + 4 * q;
+        const int row = 4 * h + j + 8 * part;
+        off[part][db] = TileFmt<D>::off(row, col >> 3) + ((col & 4) << 1);
+      }
+  }
+};
+
+// An LDS byte address held in a VGPR that the optimiser cannot see through:
+// offsets added to it afterwards can only become the instruction's immediate
+// offset field (this keeps per-read address arithmetic out of the loops).
+__device__ __forceinline__ const lds_char* lds_base(const lds_char* tile, int byte_off) {
+  uint32_t a = uint32_t(reinterpret_cast<uintptr_t>(tile)) + uint32_t(byte_off);
+  __asm__("" : "+v"(a));
+  return reinterpret_cast<const lds_char*>(uintptr_t(a));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_rows_at(const lds_char* tile, int byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(tile + byte_off);
+}
+
+__device__ __forceinline__ bf16x8_t frag_tr_at(const lds_char* tile, int off0, int off1) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off0));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off1));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Transposed fragment from two precomputed bases plus a shared immediate.
+__device__ __forceinline__ bf16x8_t frag_tr2(const lds_char* b0, const lds_char* b1, int imm) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b0 + imm));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b1 + imm));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 }  // namespace uly
