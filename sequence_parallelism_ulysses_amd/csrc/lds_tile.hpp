@@ -49,16 +49,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Issue the asynchronous copy of one tile: rows [0, 64) of a tensor whose
+// The same, with both arguments moved to scalar registers (they must be
+// wave-uniform), as inline assembly operands require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  // readfirstlane works on int: widen through uint32_t, never sign-extend
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)));
+  const uint64_t ub = (uint64_t(hi) << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ub), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Asynchronous global -> LDS copy of kBytes (4 or 16) per lane: lane l's data
+// lands at lds_wave_base + kBytes * l. Written as inline assembly, so the
+// compiler does not know about the copy: it neither orders later LDS reads
+// after it nor waits for it anywhere. The caller must wait for completion
+// (vmcnt) and synchronise (barrier) before anyone reads the destination, and
+// the resource must come from make_rsrc_uniform. M0, which holds the LDS base
+// of the copy, is restored afterwards.
+template <int kBytes>
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rsrc, const lds_char* lds_wave_base,
+                                           uint32_t voffset) {
+  static_assert(kBytes == 4 || kBytes == 16, "copy width");
+  const uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds_wave_base))));
+  uint32_t saved;
+  if constexpr (kBytes == 16)
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(m), "v"(voffset), "s"(rsrc) : "memory");
+  else
+    __asm__ volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(m), "v"(voffset), "s"(rsrc) : "memory");
+}
+
+// Issue the asynchronous copy of one tile: rows [0, ROWS) of a tensor whose
 // row r, head slice starts at byte r*row_stride from the resource base
-// (rows past the resource's range read as zero). NT threads each issue
-// 64*D*2/16/NT loads of 16 bytes; returns nothing, completion is counted by
-// vmcnt in issue order.
-template <int D, int NT>
+// (rows past the resource's range read as zero). NT threads (tid in [0, NT))
+// each issue ROWS*D*2/16/NT loads of 16 bytes; returns nothing, completion is
+// counted by vmcnt in issue order. The row layout is that of TileFmt<D>
+// whatever the number of rows.
+// kOpaque: issue through dma_to_lds (rsrc from make_rsrc_uniform).
+template <int D, int NT, int ROWS = 64, bool kOpaque = false>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t row_stride, lds_char* tile, int tid) {
   using F = TileFmt<D>;
-  constexpr int kLoads = F::kRows * F::kChunks / NT;
-  static_assert(F::kRows * F::kChunks % NT == 0, "tile split");
+  constexpr int kLoads = ROWS * F::kChunks / NT;
+  static_assert(ROWS * F::kChunks % NT == 0 && kLoads > 0, "tile split");
   const int lane = tid & 63, wave_base = tid & ~63;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
@@ -67,13 +106,16 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t
     const int chunk = (slot % F::kChunks) ^ F::swz(row);  // logical chunk stored at this slot
     lds_char* dst = tile + 16 * (NT * i + wave_base);     // wave-uniform base; lane adds 16*lane
     (void)lane;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16,
-                                             row * row_stride + chunk * 16, 0, 0, 0);
+    if constexpr (kOpaque)
+      dma_to_lds<16>(rsrc, dst, row * row_stride + chunk * 16);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               row * row_stride + chunk * 16, 0, 0, 0);
   }
 }
 
-template <int D, int NT>
-constexpr int tile_loads() { return 64 * (D / 8) / NT; }
+template <int D, int NT, int ROWS = 64>
+constexpr int tile_loads() { return ROWS * (D / 8) / NT; }
 
 // Wait until at most `n` vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; exp/lgkm counters
