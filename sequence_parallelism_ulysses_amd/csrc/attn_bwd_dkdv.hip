@@ -8,9 +8,11 @@
 //       the staged tile, B: this lane's K and V rows, held in registers),
 //       then P = exp(S - LSE) and dS = P (dP - Delta) on the vector unit;
 //       P and dS go to LDS as ready-made MFMA B fragments;
-//   consumer wave kb + 4:    dV^T += dO^T P and dK^T += Q^T dS (A:
-//       ds_read_b64_tr_b16 of the staged Q / dO tile, B: the fragments), one
-//       tile behind the producer, accumulating in registers.
+//   consumer waves 4-7:      wave 4 + 2j + r accumulates dV^T += dO^T P
+//       (r = 0) or dK^T += Q^T dS (r = 1) for the 64 keys of blocks 2j and
+//       2j + 1 (A: ds_read_b64_tr_b16 of the staged dO / Q tile, each read
+//       feeding both blocks; B: the fragments), one tile behind the
+//       producers, accumulating in registers.
 // So while one wave of a SIMD is busy with exponentials the other has matrix
 // work, and neither needs registers for both the K/V rows and the dK/dV
 // accumulators. The consumers also issue the tile copies (a four-stage ring,
@@ -61,7 +63,6 @@ void dkdv_bf16_kernel(BwdParams p) {
   const int split = int(blockIdx.x) % p.splits;
   const int kv0 = (int(blockIdx.x) / p.splits) * C::kKeys;  // first tiles carry the most causal work
   const int kw0 = kv0 + 32 * kb;
-  const bool active = kw0 < p.N;
   const int key = kw0 + l32;
   const int my_de = doc_of(p.cu, p.ndocs, p.N, min(key, p.N - 1)).end;
   const int w_de_first = doc_of(p.cu, p.ndocs, p.N, min(kw0, p.N - 1)).end;
@@ -81,14 +82,16 @@ void dkdv_bf16_kernel(BwdParams p) {
   auto tile_q0 = [&](int it) { return (qt0 + it % n_qt) * C::QT; };
   auto tile_head = [&](int it) { return kvh * p.G + it / n_qt; };
   auto stage = [&](int it) { return ring + ((it - it0) % C::NSTAGE) * C::STAGE; };
-  // does this wave's key block receive gradient from tile it?
-  auto sees = [&](int it) {
+  // does a key block (first key kb0, its documents ending by de_last) receive
+  // gradient from tile it?
+  auto sees_block = [&](int it, int kb0, int de_last) {
     const int qs = tile_q0(it);
-    return active && qs + C::QT - 1 >= kw0 && qs < w_de_last;
+    return kb0 < p.N && qs + C::QT - 1 >= kb0 && qs < de_last;
   };
-  // P (slots 0, 1) and dS (slots 2, 3) fragments of tile it for this key block
-  auto pds_at = [&](int it, int slot) {
-    return pds + (((it & 1) * 4 + kb) * 4 + slot) * 1024 + lane * 16;
+  auto sees = [&](int it) { return sees_block(it, kw0, w_de_last); };
+  // P (slots 0, 1) and dS (slots 2, 3) fragments of tile it for key block b
+  auto pds_at = [&](int it, int b, int slot) {
+    return pds + (((it & 1) * 4 + b) * 4 + slot) * 1024 + lane * 16;
   };
   typedef __attribute__((address_space(3))) bf16x8_t lds_frag;
 
@@ -157,21 +160,37 @@ void dkdv_bf16_kernel(BwdParams p) {
           }
 #pragma unroll
           for (int st2 = 0; st2 < 2; ++st2) {
-            *(lds_frag*)pds_at(it, st2) = make_frag<TrBF16>(&pv[st2 * 8]);
-            *(lds_frag*)pds_at(it, 2 + st2) = make_frag<TrBF16>(&dsv[st2 * 8]);
+            *(lds_frag*)pds_at(it, kb, st2) = make_frag<TrBF16>(&pv[st2 * 8]);
+            *(lds_frag*)pds_at(it, kb, 2 + st2) = make_frag<TrBF16>(&dsv[st2 * 8]);
           }
         };
         // the element-wise mask only on diagonal tiles and tiles crossing a document end
         if (need_mask) probs(std::true_type{}); else probs(std::false_type{});
+      } else if (it < it1) {
+        // a consumer covers two key blocks and may still read this one's fragments
+#pragma unroll
+        for (int slot = 0; slot < 4; ++slot) *(lds_frag*)pds_at(it, kb, slot) = bf16x8_t{};
       }
     }
     return;
   }
 
-  // consumer: dV^T += dO^T P ; dK^T += Q^T dS over the 32 queries of each tile
-  f32x16_t dkt[C::DB], dvt[C::DB];
+  // consumer: dV^T += dO^T P (dk_role false) or dK^T += Q^T dS (true) over
+  // the 32 queries of each tile, for key blocks cb and cb + 1
+  const int cw = w - 4;
+  const bool dk_role = cw & 1;
+  const int cb = 2 * (cw >> 1);
+  int cb_k0[2], cb_de[2];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) dkt[db] = dvt[db] = f32x16_t{};
+  for (int b = 0; b < 2; ++b) {
+    cb_k0[b] = kv0 + 32 * (cb + b);
+    cb_de[b] = doc_of(p.cu, p.ndocs, p.N, min(cb_k0[b] + 31, p.N - 1)).end;
+  }
+  f32x16_t acc[2][C::DB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[b][db] = f32x16_t{};
   TrFragOffsets<D> to;  // transposed reads over 16-row steps
   to.init(lane);
   const int ctid = tid - C::kProducers;
@@ -191,6 +210,8 @@ void dkdv_bf16_kernel(BwdParams p) {
   };
   if (it0 < it1) issue(it0);
   if (it0 + 1 < it1) issue(it0 + 1);
+  const int slot0 = dk_role ? 2 : 0;          // dS or P fragments
+  const int src_off = dk_role ? 0 : C::TQ;    // Q or dO tile
   for (int it = it0; it <= it1; ++it) {
     // tile it must have landed before the barrier; it+1 may be in flight
     if (it + 1 < it1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
@@ -198,58 +219,56 @@ void dkdv_bf16_kernel(BwdParams p) {
     // the stage of tile it-2 is free: its consumer pass ended last iteration
     if (it + 2 < it1) issue(it + 2);
     const int jt = it - 1;  // the tile the producers finished last iteration
-    if (jt >= it0 && sees(jt)) {
-      const lds_char* qt = stage(jt);
-      const lds_char* dt = qt + C::TQ;
+    if (jt >= it0 && (sees_block(jt, cb_k0[0], cb_de[0]) || sees_block(jt, cb_k0[1], cb_de[1]))) {
+      const lds_char* src = stage(jt) + src_off;
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2) {
-        const bf16x8_t pf = *(const lds_frag*)pds_at(jt, st2);
-        const bf16x8_t sf = *(const lds_frag*)pds_at(jt, 2 + st2);
+        const bf16x8_t f0 = *(const lds_frag*)pds_at(jt, cb, slot0 + st2);
+        const bf16x8_t f1 = *(const lds_frag*)pds_at(jt, cb + 1, slot0 + st2);
         const int k0 = 16 * st2 * C::RB;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          dvt[db] = mfma(frag_tr_at(dt, to.off[0][db] + k0, to.off[1][db] + k0), pf, dvt[db]);
-          dkt[db] = mfma(frag_tr_at(qt, to.off[0][db] + k0, to.off[1][db] + k0), sf, dkt[db]);
+          const bf16x8_t a = frag_tr_at(src, to.off[0][db] + k0, to.off[1][db] + k0);
+          acc[0][db] = mfma(a, f0, acc[0][db]);
+          acc[1][db] = mfma(a, f1, acc[1][db]);
         }
       }
     }
   }
 
-  // Epilogue: lane (key, half) holds d = 32 db + acc_row(r, half).
-  if (p.splits > 1) {
-    // fp32 partial sums, reduced in split order by dkdv_reduce_kernel
-    if (active && key < p.N) {
-      const int64_t off = ((int64_t(split) * p.N + key) * p.hk + kvh) * D;
+  // Epilogue: lane (key, half) of block b holds d = 32 db + acc_row(r, half).
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int bkey = cb_k0[b] + l32;
+    if (bkey >= p.N) continue;
+    if (p.splits > 1) {
+      // fp32 partial sums, reduced in split order by dkdv_reduce_kernel
+      float* part = dk_role ? p.part_dk : p.part_dv;
+      const int64_t off = ((int64_t(split) * p.N + bkey) * p.hk + kvh) * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d = db * 32 + 8 * r4 + 4 * half;
-          *reinterpret_cast<f32x4_t*>(p.part_dk + off + d) =
-              f32x4_t{dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2], dkt[db][4 * r4 + 3]};
-          *reinterpret_cast<f32x4_t*>(p.part_dv + off + d) =
-              f32x4_t{dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]};
+          *reinterpret_cast<f32x4_t*>(part + off + d) =
+              f32x4_t{acc[b][db][4 * r4], acc[b][db][4 * r4 + 1], acc[b][db][4 * r4 + 2], acc[b][db][4 * r4 + 3]};
+        }
+    } else {
+      constexpr int OE = kF32Out ? 4 : 2;
+      char* out = dk_role ? p.dk : p.dv;
+      const float mul = dk_role ? p.scale : 1.f;
+      const int64_t off = (int64_t(bkey) * p.hk + kvh) * D * OE;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * half;
+          float x[4];
+#pragma unroll
+          for (int j2 = 0; j2 < 4; ++j2) x[j2] = acc[b][db][4 * r4 + j2] * mul;
+          store4<kF32Out>(out + off + d * OE, x);
         }
     }
-    return;
-  }
-  if (active && key < p.N) {
-    constexpr int OE = kF32Out ? 4 : 2;
-    const int64_t off = (int64_t(key) * p.hk + kvh) * D * OE;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = db * 32 + 8 * r4 + 4 * half;
-        float kx[4], vx[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kx[j] = dkt[db][4 * r4 + j] * p.scale;
-          vx[j] = dvt[db][4 * r4 + j];
-        }
-        store4<kF32Out>(p.dk + off + d * OE, kx);
-        store4<kF32Out>(p.dv + off + d * OE, vx);
-      }
   }
 }
 
