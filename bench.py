@@ -13,11 +13,14 @@ Metric: algorithmic causal-attention fwd+bwd TFLOP/s of the step
 roofline of the dominant call and the oracle timed on the host as a baseline.
 Prints one JSON line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+       python bench.py --copy-calibration   (a plain 1 GiB device copy, for
+                                             scaling rocprofv3 byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -80,6 +83,49 @@ def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
                       f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}"}
 
 
+def source_digest() -> str:
+    """sha256 over the HIP sources and the C header: HBM-traffic figures
+    measured with rocprofv3 counters are reported only for the sources they
+    were measured on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sequence_parallelism_ulysses_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "ulysses.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attn_bwd call from profiles/traffic.json (FETCH_SIZE +
+    WRITE_SIZE of its launches, scaled by the same counters on a plain copy),
+    or None when absent or measured on other sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def copy_calibration() -> int:
+    """A plain device-to-device copy of 1 GiB, five times."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n, "repeats": 5}}), flush=True)
+    return 0
+
+
 def _doc_starts(N, cu):
     cuv = np.array([0, N]) if cu is None else np.asarray(cu, dtype=np.int64)
     tok = np.arange(N)
@@ -92,10 +138,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2", help="workload key: c2 (default), c3, c4, c5")
+    ap.add_argument("--config", default="c3", help="workload key: c3 (default), c2, c4, c5")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the path on a single GPU; "
@@ -195,7 +244,8 @@ def main() -> int:
     roofline = {
         "kernel": dom + (" (delta + dkdv + dq launches)" if dom == "attn_bwd" else ""),
         "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": measured_traffic(cfg.workload) if dom == "attn_bwd" else None,
         "per_launch": f"{'10' if dom == 'attn_bwd' else '4'}*D*C*hq = {dom_flop:.4g} FLOP, "
                       f"C = {C} causal pairs, hq = {hq}, D = {D}",
         "avg_launch_ms": round(call_ms[dom], 4),
