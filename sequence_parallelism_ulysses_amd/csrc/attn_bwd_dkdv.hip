@@ -70,20 +70,22 @@ void dkdv_bf16_kernel(BwdParams p) {
   const uint32_t q_row = uint32_t(p.hq) * D * 2;
 
   // Queries that can see any of the 128 keys: [kv0, end of the last key's
-  // document). The (query tile, q head) iterations over them are split evenly
-  // between p.splits workgroups; this one takes [it0, it1). Tiles run from
-  // the last one down, heads innermost, so that the workgroups resident at
-  // the same time (which start together) stream the same Q / dO tiles and
-  // share them in L2 instead of each fetching its own from memory.
+  // document). The (query tile, q head) iterations over them, tiles from the
+  // last one down and heads innermost, are dealt round-robin to the p.splits
+  // workgroups of the key block; this one runs its share as local
+  // iterations [it0, it1). All workgroups thus walk the tiles in the same
+  // order at about the same pace, so those resident at the same time stream
+  // the same Q / dO tiles and share them in L2 instead of each fetching its
+  // own from memory.
   const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + C::kKeys - 1, p.N - 1)).end;
   const int qt0 = kv0 / C::QT;
   const int n_qt = (q_end - 1) / C::QT - qt0 + 1;
   const int n_it = n_qt * p.G;
-  const int it0 = int(int64_t(n_it) * split / p.splits);
-  const int it1 = int(int64_t(n_it) * (split + 1) / p.splits);
+  const int it0 = 0;
+  const int it1 = max(0, (n_it - split + p.splits - 1) / p.splits);
 
-  auto tile_q0 = [&](int it) { return (qt0 + n_qt - 1 - it / p.G) * C::QT; };
-  auto tile_head = [&](int it) { return kvh * p.G + it % p.G; };
+  auto tile_q0 = [&](int it) { return (qt0 + n_qt - 1 - (split + it * p.splits) / p.G) * C::QT; };
+  auto tile_head = [&](int it) { return kvh * p.G + (split + it * p.splits) % p.G; };
   auto stage = [&](int it) { return ring + ((it - it0) % C::NSTAGE) * C::STAGE; };
   // does a key block (first key kb0, its documents ending by de_last) receive
   // gradient from tile it?
