@@ -20,7 +20,7 @@ namespace uly {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = 4;
+constexpr int kItems = 4;  // 16-byte chunks per thread (the fast path is written for 4)
 
 struct PermuteArgs {
   char* shard[ULY_MAX_P];
@@ -38,32 +38,32 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   const uint32_t n_chunks = a.T * a.chunks_per_row;  // < 2^31, checked on the host
   char* shard = a.shard[j];
   char* packed = a.packed + (uint64_t)j * a.T * a.seg_bytes;
-  const uint32_t base = blockIdx.x * (kThreads * kItems) + threadIdx.x;
+  const uint32_t first = blockIdx.x * (kThreads * kItems);
+  const uint32_t base = first + threadIdx.x;
 
-  uint4 buf[kItems];
-  uint64_t shard_off[kItems];
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const uint32_t i = base + it * kThreads;
+  auto shard_off = [&](uint32_t i) {
     const uint32_t t = i / a.chunks_per_row;
     const uint32_t c = i - t * a.chunks_per_row;
-    shard_off[it] = (uint64_t)t * a.row_bytes + a.head_offset + 16ull * c;
-  }
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const uint32_t i = base + it * kThreads;
-    if (i < n_chunks) {
-      const char* src = kPack ? shard + shard_off[it] : packed + 16ull * i;
-      buf[it] = *reinterpret_cast<const uint4*>(src);
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const uint32_t i = base + it * kThreads;
-    if (i < n_chunks) {
-      char* dst = kPack ? packed + 16ull * i : shard + shard_off[it];
-      *reinterpret_cast<uint4*>(dst) = buf[it];
-    }
+    return (uint64_t)t * a.row_bytes + a.head_offset + 16ull * c;
+  };
+  auto src_of = [&](uint32_t i) -> const uint4* {
+    return reinterpret_cast<const uint4*>(kPack ? shard + shard_off(i) : packed + 16ull * i);
+  };
+  auto dst_of = [&](uint32_t i) -> uint4* {
+    return reinterpret_cast<uint4*>(kPack ? packed + 16ull * i : shard + shard_off(i));
+  };
+
+  if (first + kThreads * kItems <= n_chunks) {
+    // whole block in range: all kItems loads in flight before the first store
+    // (plain registers; a guarded array here ends up staged through LDS)
+    uint4 v0 = *src_of(base), v1 = *src_of(base + kThreads), v2 = *src_of(base + 2 * kThreads),
+          v3 = *src_of(base + 3 * kThreads);
+    *dst_of(base) = v0;
+    *dst_of(base + kThreads) = v1;
+    *dst_of(base + 2 * kThreads) = v2;
+    *dst_of(base + 3 * kThreads) = v3;
+  } else {
+    for (uint32_t i = base; i < n_chunks; i += kThreads) *dst_of(i) = *src_of(i);
   }
 }
 
