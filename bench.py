@@ -83,13 +83,17 @@ def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
                       f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}"}
 
 
+# The sources of the attn_bwd call's kernels (and what they include).
+BWD_SOURCES = ("attn_bwd.hip", "attn_bwd_dkdv.hip", "bwd_common.hpp", "lds_tile.hpp", "common.hpp", "internal.hpp")
+
+
 def source_digest() -> str:
-    """sha256 over the HIP sources and the C header: HBM-traffic figures
-    measured with rocprofv3 counters are reported only for the sources they
-    were measured on."""
+    """sha256 over the backward's HIP sources and the C header: HBM-traffic
+    figures measured with rocprofv3 counters are reported only for the
+    sources they were measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sequence_parallelism_ulysses_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "ulysses.h")]
+    files = [os.path.join(csrc, f) for f in BWD_SOURCES] + [os.path.join(ROOT, "include", "ulysses.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
