@@ -334,10 +334,15 @@ void attn_fwd_kernel(FwdParams p) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel: K and V tiles stay row-major in LDS (swizzled, see
-// lds_tile.hpp), filled by asynchronous buffer loads into a three-stage ring
-// (tile t+2 in flight while tile t is consumed, one barrier per tile); V^T
-// operands come from ds_read_b64_tr_b16. No register staging, no transposing
-// stores.
+// lds_tile.hpp), filled by asynchronous buffer loads into a four-stage ring;
+// V^T operands come from ds_read_b64_tr_b16. No register staging, no
+// transposing stores.
+//
+// The two waves of a SIMD (w and w + 4) run half an iteration apart: each
+// key tile takes two phases separated by barriers, and in each phase one of
+// them issues the products S = K Q^T while the other runs the softmax and
+// O += V P of the tile before, so the matrix unit has work while the other
+// wave's exponentials run.
 // ---------------------------------------------------------------------------
 template <int D>
 struct FwdBf {
@@ -348,7 +353,8 @@ struct FwdBf {
   static constexpr int TB = TileFmt<D>::kBytes;
   static constexpr int STAGE = 2 * TB;  // K tile, V tile
   static constexpr int NSTAGE = 4;
-  static constexpr int LOADS = 2 * tile_loads<D, kThreads>();  // per thread per stage
+  static constexpr int kCopiers = kThreads / 2;  // waves 4-7 issue the tile copies
+  static constexpr int LOADS = 2 * tile_loads<D, kCopiers>();  // per copying lane per stage
 };
 
 template <int D>
@@ -398,19 +404,22 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const int t0 = kv_begin / BN, t1 = (wg_q1 - 1) / BN;
   const uint32_t kv_row = uint32_t(p.hk) * D * 2;
 
+  // Group A (waves 0-3) runs tile t's products in the first phase of
+  // iteration t and its softmax in the second; group B (waves 4-7) the
+  // products in the second phase and the softmax in the first phase of
+  // iteration t+1. Group B also issues the tile copies (inline-assembly DMA,
+  // so that the compiler does not make its transposed LDS reads wait for
+  // them) and waits for them before the first barrier of each iteration.
+  const bool grp_b = w >= C::kWaves / 2;
+  const int btid = tid - C::kCopiers;
   auto issue = [&](int t) {
     lds_char* st = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
     const int kv0 = t * BN;
     const uint32_t bytes = uint32_t(min(BN, p.N - kv0)) * kv_row;
     const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
-    issue_tile<D, C::kThreads>(make_rsrc(p.k + off, bytes), kv_row, st, tid);
-    issue_tile<D, C::kThreads>(make_rsrc(p.v + off, bytes), kv_row, st + C::TB, tid);
+    issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform(p.k + off, bytes), kv_row, st, btid);
+    issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform(p.v + off, bytes), kv_row, st + C::TB, btid);
   };
-  // Software pipeline over key tiles: while the softmax of tile t runs on the
-  // VALU, the MFMAs of S(t+1) = K(t+1) Q^T are already in flight, so each
-  // wave has independent matrix work during its exponentials. K(t+1) must be
-  // resident one tile early; a four-stage ring keeps two tiles of copies in
-  // flight behind it.
   auto sees = [&](int t) {
     const int kv0 = t * BN;
     return active && kv0 <= wq_last && kv0 + BN > w_ds_first;
@@ -427,83 +436,89 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  for (int i = 0; i < 3; ++i)
-    if (t0 + i <= t1) issue(t0 + i);
-  if (t0 + 2 <= t1) wait_vmcnt<2 * C::LOADS>(); else if (t0 + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
-  __syncthreads();
-  f32x16_t s_cur[2], s_nxt[2];
-  if (sees(t0)) compute_s(t0, s_cur);
-
-  for (int t = t0; t <= t1; ++t) {
-    // tile t+1 (its K feeds S(t+1) now) must have landed; t+2 may be in flight
-    if (t + 2 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
-    __syncthreads();  // everyone's copies landed; stage t-1 is free
+  // mask, online softmax and O^T += V^T P^T for tile t, S(t) in s
+  auto softmax_pv = [&](int t, f32x16_t (&s)[2]) {
     const int kv0 = t * BN;
     const lds_char* lv = smem + ((t - t0) % C::NSTAGE) * C::STAGE + C::TB;
-    const bool next = t + 1 <= t1 && sees(t + 1);
-    if (next) compute_s(t + 1, s_nxt);
-
-    if (sees(t)) {
-      f32x16_t (&s)[2] = s_cur;
-      // element-wise mask only on the diagonal tile and tiles crossing a document start
-      const bool need_mask = kv0 + BN - 1 > qbase || kv0 < w_ds_last;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + acc_row(r, half);
-            if (key > my_q || key < my_ds) s[kb][r] = -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = xhalf_max(mt) * p.scale_log2;
-      // raise the running max only when the tile's max exceeds it by > 2^8
-      const bool grow = mt > m + kRescaleLog2;
-      if (wave_any(grow)) {
-        const float alpha = grow ? fast_exp2(m - mt) : 1.f;  // 0 when m was -inf
-        m = grow ? mt : m;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc_o[db] *= alpha;
-      }
-      const float m_use = m == -INFINITY ? 0.f : m;
-      float pv[32];
+    // element-wise mask only on the diagonal tile and tiles crossing a document start
+    const bool need_mask = kv0 + BN - 1 > qbase || kv0 < w_ds_last;
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -m_use));
-          pv[kb * 16 + r] = e;
-          l += e;
+          const int key = kv0 + kb * 32 + acc_row(r, half);
+          if (key > my_q || key < my_ds) s[kb][r] = -INFINITY;
         }
-      // O^T += V^T P^T, 16 keys per step; V^T read transposed from the row-major tile
-      const lds_char* va[2][C::DB];
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        va[0][db] = lds_base(lv, vo.off[0][db]);
-        va[1][db] = lds_base(lv, vo.off[1][db]);
-      }
-#pragma unroll
-      for (int st = 0; st < BN / 16; ++st) {
-        const bf16x8_t pf = make_frag<TrBF16>(&pv[st * 8]);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc_o[db] = mfma(frag_tr2(va[0][db], va[1][db], st * 32 * D), pf, acc_o[db]);
-      }
     }
-    if (next) {
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = xhalf_max(mt) * p.scale_log2;
+    // raise the running max only when the tile's max exceeds it by > 2^8
+    const bool grow = mt > m + kRescaleLog2;
+    if (wave_any(grow)) {
+      const float alpha = grow ? fast_exp2(m - mt) : 1.f;  // 0 when m was -inf
+      m = grow ? mt : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc_o[db] *= alpha;
     }
-    // Refill the stage every wave finished with (tile t-1) only after this
-    // tile's LDS reads: the compiler waits for all in-flight LDS copies
-    // before transposed LDS reads.
-    if (t + 3 <= t1) issue(t + 3);
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float pv[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -m_use));
+        pv[kb * 16 + r] = e;
+        l += e;
+      }
+    // O^T += V^T P^T, 16 keys per step; V^T read transposed from the row-major tile
+    const lds_char* va[2][C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      va[0][db] = lds_base(lv, vo.off[0][db]);
+      va[1][db] = lds_base(lv, vo.off[1][db]);
+    }
+#pragma unroll
+    for (int st = 0; st < BN / 16; ++st) {
+      const bf16x8_t pf = make_frag<TrBF16>(&pv[st * 8]);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        acc_o[db] = mfma(frag_tr2(va[0][db], va[1][db], st * 32 * D), pf, acc_o[db]);
+    }
+  };
+
+  // One loop per group (the barrier counts match), so that each keeps only
+  // its own values in registers.
+  f32x16_t s[2];
+  if (!grp_b) {
+    for (int t = t0; t <= t1 + 1; ++t) {
+      __syncthreads();  // tile t has landed (group B waited for it)
+      if (t <= t1 && sees(t)) compute_s(t, s);
+      __syncthreads();
+      if (t <= t1 && sees(t)) softmax_pv(t, s);
+    }
+  } else {
+    for (int i = 0; i < 3; ++i)
+      if (t0 + i <= t1) issue(t0 + i);
+    for (int t = t0; t <= t1 + 1; ++t) {
+      if (t <= t1) {
+        // tile t must have landed; the copies of up to two later tiles may be in flight
+        const int ahead = min(2, t1 - t);
+        if (ahead == 2) wait_vmcnt<2 * C::LOADS>(); else if (ahead == 1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
+      }
+      __syncthreads();
+      if (t - 1 >= t0 && sees(t - 1)) softmax_pv(t - 1, s);
+      __syncthreads();
+      if (t <= t1 && sees(t)) compute_s(t, s);
+      // the stage of tile t-1 is free: its last reader was this group's
+      // softmax of it, before the second barrier
+      if (t + 3 <= t1) issue(t + 3);
+    }
   }
 
   const float lsum = xhalf_sum(l);
