@@ -353,8 +353,8 @@ struct FwdBf {
   static constexpr int TB = TileFmt<D>::kBytes;
   static constexpr int STAGE = 2 * TB;  // K tile, V tile
   static constexpr int NSTAGE = 4;
-  static constexpr int kCopiers = kThreads / 2;  // waves 4-7 issue the tile copies
-  static constexpr int LOADS = 2 * tile_loads<D, kCopiers>();  // per copying lane per stage
+  static constexpr int kCopiers = kThreads / 2;  // one group of four waves copies one tensor
+  static constexpr int LOADS = tile_loads<D, kCopiers>();  // per copying lane per stage
 };
 
 template <int D>
@@ -407,18 +407,25 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // Group A (waves 0-3) runs tile t's products in the first phase of
   // iteration t and its softmax in the second; group B (waves 4-7) the
   // products in the second phase and the softmax in the first phase of
-  // iteration t+1. Group B also issues the tile copies (inline-assembly DMA,
-  // so that the compiler does not make its transposed LDS reads wait for
-  // them) and waits for them before the first barrier of each iteration.
+  // iteration t+1. Each group copies one tensor of tile t+3 after its
+  // products (A the K tile, B the V tile), where the copies' stall at the
+  // address unit costs least; the copies are inline-assembly DMA, so that
+  // the compiler does not make transposed LDS reads wait for them, and each
+  // group waits for its own before the first barrier of an iteration.
   const bool grp_b = w >= C::kWaves / 2;
-  const int btid = tid - C::kCopiers;
-  auto issue = [&](int t) {
+  const int gtid = tid & (C::kCopiers - 1);
+  auto issue = [&](int t, bool v_tile) {
     lds_char* st = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
     const int kv0 = t * BN;
     const uint32_t bytes = uint32_t(min(BN, p.N - kv0)) * kv_row;
     const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
-    issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform(p.k + off, bytes), kv_row, st, btid);
-    issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform(p.v + off, bytes), kv_row, st + C::TB, btid);
+    issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform((v_tile ? p.v : p.k) + off, bytes), kv_row,
+                                         st + (v_tile ? C::TB : 0), gtid);
+  };
+  // tile t must have landed; this group's copies of up to two later tiles may be in flight
+  auto wait_tile = [&](int t) {
+    const int ahead = min(2, t1 - t);
+    if (ahead == 2) wait_vmcnt<2 * C::LOADS>(); else if (ahead == 1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
   };
   auto sees = [&](int t) {
     const int kv0 = t * BN;
@@ -495,29 +502,29 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // One loop per group (the barrier counts match), so that each keeps only
   // its own values in registers.
   f32x16_t s[2];
+  for (int i = 0; i < 3; ++i)
+    if (t0 + i <= t1) issue(t0 + i, grp_b);
   if (!grp_b) {
     for (int t = t0; t <= t1 + 1; ++t) {
-      __syncthreads();  // tile t has landed (group B waited for it)
+      if (t <= t1) wait_tile(t);
+      __syncthreads();
       if (t <= t1 && sees(t)) compute_s(t, s);
+      // K of tile t-1 was last read by group B's products in the previous
+      // iteration's second phase
+      if (t + 3 <= t1) issue(t + 3, false);
       __syncthreads();
       if (t <= t1 && sees(t)) softmax_pv(t, s);
     }
   } else {
-    for (int i = 0; i < 3; ++i)
-      if (t0 + i <= t1) issue(t0 + i);
     for (int t = t0; t <= t1 + 1; ++t) {
-      if (t <= t1) {
-        // tile t must have landed; the copies of up to two later tiles may be in flight
-        const int ahead = min(2, t1 - t);
-        if (ahead == 2) wait_vmcnt<2 * C::LOADS>(); else if (ahead == 1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
-      }
+      if (t <= t1) wait_tile(t);
       __syncthreads();
       if (t - 1 >= t0 && sees(t - 1)) softmax_pv(t - 1, s);
       __syncthreads();
       if (t <= t1 && sees(t)) compute_s(t, s);
-      // the stage of tile t-1 is free: its last reader was this group's
-      // softmax of it, before the second barrier
-      if (t + 3 <= t1) issue(t + 3);
+      // V of tile t-1 was last read by this group's softmax of it, before
+      // the second barrier
+      if (t + 3 <= t1) issue(t + 3, true);
     }
   }
 
