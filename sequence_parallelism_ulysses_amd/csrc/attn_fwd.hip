@@ -435,12 +435,20 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     const lds_char* lk = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
     s[0] = f32x16_t{};
     s[1] = f32x16_t{};
+    // all K reads of the tile go out before the first product, so the
+    // products run back to back rather than each waiting on its own read
+    bf16x8_t kf[C::KS][2];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const lds_char* ka = lds_base(lk, ko.off[ks]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(frag_rows_at<D>(ka, kb * 64 * D), qf[ks], s[kb]);
+      for (int kb = 0; kb < 2; ++kb) kf[ks][kb] = frag_rows_at<D>(ka, kb * 64 * D);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(kf[ks][kb], qf[ks], s[kb]);
   };
 
   // mask, online softmax and O^T += V^T P^T for tile t, S(t) in s
