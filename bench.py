@@ -169,8 +169,12 @@ def main() -> int:
     cu = syn.cu_seqlens(cfg)
     cu_dev = None if cu is None else torch.from_numpy(cu).to(dev)
 
-    host = {n: syn.all_shards_bits(cfg, n) for n in ("q", "k", "v", "do")}
-    shards = {n: [torch.from_numpy(s.view(np.int16)).to(dev).view(tdt) for s in host[n]] for n in host}
+    host, shards = {}, {}
+    for n in ("q", "k", "v", "do"):
+        # progress on stderr: the million-token inputs take minutes to generate
+        print(f"bench: generating {n} shards of {cfg.workload}", file=sys.stderr, flush=True)
+        host[n] = syn.all_shards_bits(cfg, n)
+        shards[n] = [torch.from_numpy(s.view(np.int16)).to(dev).view(tdt) for s in host[n]]
     N, hq, hk, D, P, T, g = cfg.N, cfg.hq, cfg.hk, cfg.D, cfg.P, cfg.T, cfg.group
     qg = torch.empty((N, hq, D), dtype=tdt, device=dev)
     kg = torch.empty((N, hk, D), dtype=tdt, device=dev)
