@@ -10,23 +10,27 @@
 //   dV_j = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 //
 // Three kernels, all deterministic (no atomics):
-//   1. delta: one row dot product per (query, head).
-//   2. dK/dV, key-stationary: a workgroup owns 128 keys of one kv head (32 per
-//      wave, K and V held in registers), walks the query tiles that can see
-//      them for every q head of the group, and sums the GQA heads in its
-//      accumulators. Per wave and 64-query tile:
+//   1. delta: one row dot product per (query, head), and lse * log2(e).
+//   2. dK/dV, key-stationary: a workgroup owns 128 keys of one kv head, walks
+//      the query tiles that can see them for every q head of the group, and
+//      sums the GQA heads in its accumulators:
 //        S  = Q K^T, dP = dO V^T   (A operand: Q/dO rows from LDS)
 //        dV^T += dO^T P, dK^T += Q^T dS   (A operand: transposed Q/dO tiles)
-//      The S/dP accumulators hold one key column per lane, which is exactly
-//      the B-operand layout the second pair of products needs.
+//      The S/dP accumulators hold one key column per lane, which is the
+//      B-operand layout the second pair of products needs. fp32 (this file):
+//      4 waves of 32 keys, each doing all four products, on 64-query tiles.
+//      bf16 (attn_bwd_dkdv.hip): 8 waves on 32-query tiles, split into
+//      producers (S, dP, P, dS) and consumers (dV or dK) that pass P and dS
+//      through LDS. With splits > 1 several workgroups share a key block and
+//      write fp32 partials that dkdv_reduce_kernel adds in split order.
 //   3. dQ, query-stationary: like the forward, a wave owns 32 query rows and
 //      walks the key tiles: S^T = K Q^T, dP^T = V dO^T, then
-//      dQ^T += K^T dS^T from a transposed K tile.
+//      dQ^T += K^T dS^T from a transposed K operand.
 //
-// LDS tiles (bf16) are stored twice, row-major and transposed, from one
-// global load. Both layouts use an XOR swizzle of the 16-byte chunk index so
-// that MFMA operand reads (8 consecutive rows per access phase) and the
-// transposing stores stay bank-conflict free or nearly so.
+// Tiles: fp32 tiles are staged through registers into padded LDS rows (the
+// transposed operand stored a second time); bf16 tiles are copied global ->
+// LDS by buffer loads into row-major, XOR-swizzled rows (lds_tile.hpp) and
+// the transposed operands are read with ds_read_b64_tr_b16.
 #include <cmath>
 #include <numeric>
 
@@ -65,44 +69,7 @@ WsLayout ws_layout(const AttnDesc& d) {
   return w;
 }
 
-// ----------------------------------------------------------------------------
-// LDS layouts for bf16 tiles of BT rows x D columns.
-//   row-major   : row r at r*2D bytes, 16-byte chunk c stored at chunk c ^ (r & 7)
-//   transposed  : column d at d*2BT bytes; rows (tokens) in the order of
-//                 tr_slot() inside each 16-row group, 16-byte chunk c stored
-//                 at chunk c ^ swz(d)
-// ----------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int rm_off(int row, int chunk) {
-  return row * (2 * D) + ((chunk ^ (row & 7)) << 4);
-}
-__device__ __forceinline__ int swz(int d) { return (d ^ (d >> 3)) & 7; }
-__device__ __forceinline__ int tr_off(int d, int slot) {
-  return d * (2 * BT) + ((((slot >> 3) ^ swz(d))) << 4) + ((slot & 7) << 1);
-}
-// Position of token group g (4 consecutive tokens) inside the transposed tile:
-// order [0-3, 8-11, 4-7, 12-15] per 16 tokens, so that half-wave h reads the
-// tokens {4h..4h+3, 8+4h..8+4h+3} its accumulator-derived fragment holds.
-__device__ __forceinline__ int tr_slot(int g) {
-  const int sub = g & 3;
-  return (g >> 2) * 16 + ((sub & 1) << 3) + ((sub >> 1) << 2);
-}
-
 __device__ __forceinline__ u32x4_t ld16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-
-// Transposing store of a 4-token x 8-column block (x[i] = token 4g+i, columns
-// 8dc..8dc+7) into the transposed layout.
-__device__ __forceinline__ void store_tr(char* base, const u32x4_t (&x)[4], int g, int dc) {
-  const int slot = tr_slot(g);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w0 = x[0][j], w1 = x[1][j], w2 = x[2][j], w3 = x[3][j];
-    const u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-    const u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-    *reinterpret_cast<u32x2_t*>(base + tr_off(dc * 8 + 2 * j, slot)) = lo;
-    *reinterpret_cast<u32x2_t*>(base + tr_off(dc * 8 + 2 * j + 1, slot)) = hi;
-  }
-}
 
 // ----------------------------------------------------------------------------
 // 1. delta_i = dO_i . O_i  (fp32), for every (query, head). Each lane reads
@@ -142,28 +109,26 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdParams p) {
 // ----------------------------------------------------------------------------
 // 2. dK / dV (key-stationary)
 // ----------------------------------------------------------------------------
+// fp32 (the bf16 kernels are further down and in attn_bwd_dkdv.hip)
 template <class Tr, int D>
 struct KvCfg {
+  static_assert(Tr::kElem == 4, "fp32 kernel");
   static constexpr int E = Tr::kElem;
-  static constexpr bool kBf = (E == 2);
   static constexpr int KS = D / Tr::kStep;   // MFMA steps over D
   static constexpr int DB = D / 32;
   static constexpr int QS = BT / Tr::kStep;  // MFMA steps over the 64 queries of a tile
-  static constexpr int DC = D / 8;           // bf16: 8-column chunks per row
-  static constexpr int PAIRS = (BT / 4) * DC;
-  // f32 tiles are row-major with a 16-byte pad per row.
+  // tiles are row-major with a 16-byte pad per row; transposed operands are
+  // read element by element from them
   static constexpr int F_STRIDE = D * 4 + 16;
-  static constexpr int X_BYTES = kBf ? BT * D * 2 : BT * F_STRIDE;  // one row-major tile
-  static constexpr int T_BYTES = kBf ? BT * D * 2 : 0;              // one transposed tile
-  static constexpr int STAGE = 2 * X_BYTES + 2 * T_BYTES + 2 * BT * 4;
-  static constexpr int F_CH = BT * D * 4 / 16 / kThreads;           // f32 chunks per thread
-  static_assert(!kBf || PAIRS <= kThreads, "one pair per thread at most");
+  static constexpr int X_BYTES = BT * F_STRIDE;           // one tile
+  static constexpr int STAGE = 2 * X_BYTES + 2 * BT * 4;  // Q, dO, lse2, delta
+  static constexpr int F_CH = BT * D * 4 / 16 / kThreads;  // 16-byte chunks per thread
 };
 
 template <class Tr, int D>
 struct QTile {
   using C = KvCfg<Tr, D>;
-  static constexpr int NR = C::kBf ? 4 : C::F_CH;
+  static constexpr int NR = C::F_CH;
   u32x4_t xq[NR], xd[NR];
   float lse2, dlt;
 
@@ -171,27 +136,14 @@ struct QTile {
     const int64_t row_bytes = int64_t(p.hq) * D * C::E;
     const char* qb = p.q + int64_t(head) * D * C::E;
     const char* db = p.dout + int64_t(head) * D * C::E;
-    if constexpr (C::kBf) {
-      if (tid < C::PAIRS) {
-        const int dc = tid % C::DC, g = tid / C::DC;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = qs + 4 * g + i;
-          const bool ok = q < p.N;
-          xq[i] = ok ? ld16(qb + q * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
-          xd[i] = ok ? ld16(db + q * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c / (D / 4), col = c % (D / 4);
-        const int q = qs + row;
-        const bool ok = q < p.N;
-        xq[i] = ok ? ld16(qb + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
-        xd[i] = ok ? ld16(db + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / (D / 4), col = c % (D / 4);
+      const int q = qs + row;
+      const bool ok = q < p.N;
+      xq[i] = ok ? ld16(qb + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+      xd[i] = ok ? ld16(db + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
     }
     if (tid < BT) {
       const int q = qs + tid;
@@ -203,28 +155,13 @@ struct QTile {
   __device__ __forceinline__ void store(char* st, int tid) const {
     char* qr = st;
     char* dr = st + C::X_BYTES;
-    char* qt = st + 2 * C::X_BYTES;
-    char* dt = qt + C::T_BYTES;
-    float* fl = reinterpret_cast<float*>(st + 2 * C::X_BYTES + 2 * C::T_BYTES);
-    if constexpr (C::kBf) {
-      if (tid < C::PAIRS) {
-        const int dc = tid % C::DC, g = tid / C::DC;
+    float* fl = reinterpret_cast<float*>(st + 2 * C::X_BYTES);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4_t*>(qr + rm_off<D>(4 * g + i, dc)) = xq[i];
-          *reinterpret_cast<u32x4_t*>(dr + rm_off<D>(4 * g + i, dc)) = xd[i];
-        }
-        store_tr(qt, xq, g, dc);
-        store_tr(dt, xd, g, dc);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c / (D / 4), col = c % (D / 4);
-        *reinterpret_cast<u32x4_t*>(qr + row * C::F_STRIDE + col * 16) = xq[i];
-        *reinterpret_cast<u32x4_t*>(dr + row * C::F_STRIDE + col * 16) = xd[i];
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / (D / 4), col = c % (D / 4);
+      *reinterpret_cast<u32x4_t*>(qr + row * C::F_STRIDE + col * 16) = xq[i];
+      *reinterpret_cast<u32x4_t*>(dr + row * C::F_STRIDE + col * 16) = xd[i];
     }
     if (tid < BT) {
       fl[tid] = lse2;
@@ -291,9 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
     const char* st = smem + ((it - it0) & 1) * C::STAGE;
     const char* qr = st;
     const char* dr = st + C::X_BYTES;
-    const char* qt = st + 2 * C::X_BYTES;
-    const char* dt = qt + C::T_BYTES;
-    const float* fl = reinterpret_cast<const float*>(st + 2 * C::X_BYTES + 2 * C::T_BYTES);
+    const float* fl = reinterpret_cast<const float*>(st + 2 * C::X_BYTES);
 
     if (active && qs + BT - 1 >= kw0 && qs < w_de_last) {
       f32x16_t s[2], dp[2];
@@ -304,14 +239,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int row = qb * 32 + l32;
-          frag_t a, b;
-          if constexpr (C::kBf) {
-            a = load_frag<Tr>(qr + rm_off<D>(row, 2 * ks + half));
-            b = load_frag<Tr>(dr + rm_off<D>(row, 2 * ks + half));
-          } else {
-            a = load_frag<Tr>(qr + row * C::F_STRIDE + (2 * ks + half) * 4);
-            b = load_frag<Tr>(dr + row * C::F_STRIDE + (2 * ks + half) * 4);
-          }
+          const frag_t a = load_frag<Tr>(qr + row * C::F_STRIDE + (2 * ks + half) * 4);
+          const frag_t b = load_frag<Tr>(dr + row * C::F_STRIDE + (2 * ks + half) * 4);
           s[qb] = mfma(a, kf[ks], s[qb]);
           dp[qb] = mfma(b, vf[ks], dp[qb]);
         }
@@ -347,15 +276,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           const int d = db * 32 + l32;
-          frag_t ad, aq;
-          if constexpr (C::kBf) {
-            ad = load_frag<Tr>(dt + tr_off(d, st2 * 16 + half * 8));
-            aq = load_frag<Tr>(qt + tr_off(d, st2 * 16 + half * 8));
-          } else {
-            const int qrow = (st2 >> 4) * 32 + acc_row(st2 & 15, half);
-            ad = load_frag<Tr>(dr + qrow * C::F_STRIDE + d * 4);
-            aq = load_frag<Tr>(qr + qrow * C::F_STRIDE + d * 4);
-          }
+          const int qrow = (st2 >> 4) * 32 + acc_row(st2 & 15, half);
+          const frag_t ad = load_frag<Tr>(dr + qrow * C::F_STRIDE + d * 4);
+          const frag_t aq = load_frag<Tr>(qr + qrow * C::F_STRIDE + d * 4);
           dvt[db] = mfma(ad, pf, dvt[db]);
           dkt[db] = mfma(aq, sf, dkt[db]);
         }
@@ -435,78 +358,50 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int 
 // ----------------------------------------------------------------------------
 // 3. dQ (query-stationary)
 // ----------------------------------------------------------------------------
+// fp32
 template <class Tr, int D>
 struct QCfg {
+  static_assert(Tr::kElem == 4, "fp32 kernel");
   static constexpr int E = Tr::kElem;
-  static constexpr bool kBf = (E == 2);
   static constexpr int KS = D / Tr::kStep;
   static constexpr int DB = D / 32;
   static constexpr int PV = BT / Tr::kStep;
-  static constexpr int DC = D / 8;
-  static constexpr int PAIRS = (BT / 4) * DC;
   static constexpr int F_STRIDE = D * 4 + 16;
-  static constexpr int X_BYTES = kBf ? BT * D * 2 : BT * F_STRIDE;
-  static constexpr int T_BYTES = kBf ? BT * D * 2 : 0;
-  static constexpr int STAGE = 2 * X_BYTES + T_BYTES;  // K row-major, V row-major, K transposed
+  static constexpr int X_BYTES = BT * F_STRIDE;
+  static constexpr int STAGE = 2 * X_BYTES;  // K, V
   static constexpr int F_CH = BT * D * 4 / 16 / kThreads;
 };
 
 template <class Tr, int D>
 struct KvTile {
   using C = QCfg<Tr, D>;
-  static constexpr int NR = C::kBf ? 4 : C::F_CH;
+  static constexpr int NR = C::F_CH;
   u32x4_t xk[NR], xv[NR];
 
   __device__ __forceinline__ void load(const BwdParams& p, int kvh, int kv0, int tid) {
     const int64_t row_bytes = int64_t(p.hk) * D * C::E;
     const char* kb = p.k + int64_t(kvh) * D * C::E;
     const char* vb = p.v + int64_t(kvh) * D * C::E;
-    if constexpr (C::kBf) {
-      if (tid < C::PAIRS) {
-        const int dc = tid % C::DC, g = tid / C::DC;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kv0 + 4 * g + i;
-          const bool ok = key < p.N;
-          xk[i] = ok ? ld16(kb + key * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
-          xv[i] = ok ? ld16(vb + key * row_bytes + dc * 16) : u32x4_t{0, 0, 0, 0};
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c / (D / 4), col = c % (D / 4);
-        const int key = kv0 + row;
-        const bool ok = key < p.N;
-        xk[i] = ok ? ld16(kb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
-        xv[i] = ok ? ld16(vb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / (D / 4), col = c % (D / 4);
+      const int key = kv0 + row;
+      const bool ok = key < p.N;
+      xk[i] = ok ? ld16(kb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
+      xv[i] = ok ? ld16(vb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
     }
   }
 
   __device__ __forceinline__ void store(char* st, int tid) const {
     char* kr = st;
     char* vr = st + C::X_BYTES;
-    char* kt = st + 2 * C::X_BYTES;
-    if constexpr (C::kBf) {
-      if (tid < C::PAIRS) {
-        const int dc = tid % C::DC, g = tid / C::DC;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4_t*>(kr + rm_off<D>(4 * g + i, dc)) = xk[i];
-          *reinterpret_cast<u32x4_t*>(vr + rm_off<D>(4 * g + i, dc)) = xv[i];
-        }
-        store_tr(kt, xk, g, dc);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c / (D / 4), col = c % (D / 4);
-        *reinterpret_cast<u32x4_t*>(kr + row * C::F_STRIDE + col * 16) = xk[i];
-        *reinterpret_cast<u32x4_t*>(vr + row * C::F_STRIDE + col * 16) = xv[i];
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / (D / 4), col = c % (D / 4);
+      *reinterpret_cast<u32x4_t*>(kr + row * C::F_STRIDE + col * 16) = xk[i];
+      *reinterpret_cast<u32x4_t*>(vr + row * C::F_STRIDE + col * 16) = xv[i];
     }
   }
 };
@@ -565,7 +460,6 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
     const char* st = smem + ((t - t0) & 1) * C::STAGE;
     const char* kr = st;
     const char* vr = st + C::X_BYTES;
-    const char* kt = st + 2 * C::X_BYTES;
 
     if (active && kv0 <= wq_last && kv0 + BT > w_ds_first) {
       f32x16_t s[2], dp[2];
@@ -576,14 +470,8 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int row = kb * 32 + l32;
-          frag_t a, b;
-          if constexpr (C::kBf) {
-            a = load_frag<Tr>(kr + rm_off<D>(row, 2 * ks + half));
-            b = load_frag<Tr>(vr + rm_off<D>(row, 2 * ks + half));
-          } else {
-            a = load_frag<Tr>(kr + row * C::F_STRIDE + (2 * ks + half) * 4);
-            b = load_frag<Tr>(vr + row * C::F_STRIDE + (2 * ks + half) * 4);
-          }
+          const frag_t a = load_frag<Tr>(kr + row * C::F_STRIDE + (2 * ks + half) * 4);
+          const frag_t b = load_frag<Tr>(vr + row * C::F_STRIDE + (2 * ks + half) * 4);
           s[kb] = mfma(a, qf[ks], s[kb]);
           dp[kb] = mfma(b, df[ks], dp[kb]);
         }
@@ -608,13 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           const int d = db * 32 + l32;
-          frag_t a;
-          if constexpr (C::kBf) {
-            a = load_frag<Tr>(kt + tr_off(d, st2 * 16 + half * 8));
-          } else {
-            const int krow = (st2 >> 4) * 32 + acc_row(st2 & 15, half);
-            a = load_frag<Tr>(kr + krow * C::F_STRIDE + d * 4);
-          }
+          const int krow = (st2 >> 4) * 32 + acc_row(st2 & 15, half);
+          const frag_t a = load_frag<Tr>(kr + krow * C::F_STRIDE + d * 4);
           dqt[db] = mfma(a, sf, dqt[db]);
         }
       }

@@ -7,21 +7,21 @@
 // ...", second paragraph: each GPU runs standard attention over the full
 // sequence for its heads).
 //
-// Work decomposition (one workgroup = 4 waves):
-//   - the Gw = gcd(G, 4) q heads of one kv head that share K/V are folded
-//     into one workgroup, so each K/V tile read from HBM/L2 serves Gw heads;
-//   - every wave owns RW query rows of one q head (RW = 64 for bf16, 32 for
-//     fp32) and keeps them in registers as the MFMA B operand;
-//   - K/V tiles of 64 keys are double-buffered in LDS; global loads of tile
-//     t+2 are in flight while tile t is consumed, one barrier per tile;
-//   - workgroups are launched heaviest causal row-tile first.
+// Two kernels share the decomposition: the Gw = gcd(G, waves) q heads of
+// one kv head that share K/V are folded into one workgroup, so each K/V tile
+// read from HBM/L2 serves Gw heads; every wave owns 32 query rows of one q
+// head, held in registers as the MFMA B operand; K/V tiles hold 64 keys;
+// workgroups are launched heaviest causal row-tile first.
+//   - fp32 (attn_fwd_kernel): 4 waves, v_mfma_f32_32x32x2f32, tiles staged
+//     through registers into a double-buffered LDS pair, one barrier per tile;
+//   - bf16 (attn_fwd_bf16_kernel): 8 waves (two per SIMD, running half a tile
+//     apart), v_mfma_f32_32x32x16_bf16, tiles copied global -> LDS by buffer
+//     loads into a four-stage ring, V^T read with ds_read_b64_tr_b16.
 //
 // Per wave and tile the math runs transposed, S^T = K Q^T, so that each lane
 // owns one query column: the row max and row sum of the softmax are per-lane
 // reductions plus one v_permlane32_swap between the two half-waves. The
-// probabilities are then already laid out as the B operand of O^T += V^T P^T;
-// V^T comes from LDS, where bf16 V tiles are stored transposed (keys
-// contiguous, in the order the P fragments need).
+// probabilities are then already laid out as the B operand of O^T += V^T P^T.
 //
 // Masking (key j, query i): j <= i and j >= doc_start(i). Only the diagonal
 // tile and tiles crossing a document start are masked element-wise; tiles
@@ -51,14 +51,10 @@ struct FwdParams {
   float scale_log2;
 };
 
-// bf16: 8 waves of 32 query rows (two waves per SIMD, <= 256 registers each,
-// so one wave's softmax overlaps the other's MFMAs). fp32: 4 waves.
-template <class Tr>
-constexpr int waves_for() { return Tr::kElem == 2 ? 8 : 4; }
-
+// The fp32 kernel: 4 waves of 32 query rows.
 template <class Tr, int D>
 struct FwdCfg {
-  static constexpr int kWaves = waves_for<Tr>();
+  static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int E = Tr::kElem;
   static constexpr int QB = 1;  // 32-row blocks per wave
@@ -66,34 +62,21 @@ struct FwdCfg {
   static constexpr int KS = D / Tr::kStep;  // MFMA steps over D
   static constexpr int DB = D / 32;         // 32-wide blocks of D
   static constexpr int PV = BN / Tr::kStep; // MFMA steps over the keys of a tile
-  static constexpr bool kVt = (E == 2);     // bf16 V stored transposed in LDS
-  static constexpr int K_STRIDE = D * E + 16;
-  static constexpr int V_STRIDE = kVt ? BN * E + 16 : D * E + 16;
+  static constexpr int K_STRIDE = D * E + 16;  // rows padded by 16 bytes
+  static constexpr int V_STRIDE = D * E + 16;
   static constexpr int K_BYTES = BN * K_STRIDE;
-  static constexpr int V_BYTES = kVt ? D * V_STRIDE : BN * V_STRIDE;
-  static constexpr int CPR = D * E / 16;              // 16-byte chunks per row
-  static constexpr int K_CH = BN * CPR / kThreads;    // chunks per thread
-  static constexpr int V_PAIRS = (BN / 4) * (D / 4);  // bf16: (4-key group, 4-dim chunk)
-  static constexpr int V_REGS = kVt ? 4 : K_CH;
+  static constexpr int V_BYTES = BN * V_STRIDE;
+  static constexpr int CPR = D * E / 16;            // 16-byte chunks per row
+  static constexpr int K_CH = BN * CPR / kThreads;  // chunks per thread
   static_assert(BN * CPR % kThreads == 0, "tile must split evenly");
-  static_assert(!kVt || V_PAIRS <= kThreads, "one V pair per thread at most");
 };
-
-// Position of the 4-key group `sub` (0..3) inside a 16-key group of the
-// transposed V tile: order [keys 0-3, 8-11, 4-7, 12-15], so that half-wave h
-// reads keys {4h..4h+3, 8+4h..8+4h+3} -- the keys its P fragment holds -- as
-// one 16-byte run.
-__device__ __forceinline__ int vt_slot(int kg) {
-  const int sub = kg & 3;
-  return (kg >> 2) * 16 + ((sub & 1) << 3) + ((sub >> 1) << 2);
-}
 
 template <class Tr, int D>
 struct Tile {
   using C = FwdCfg<Tr, D>;
   static constexpr int kThreads = C::kThreads;
   u32x4_t k[C::K_CH];
-  u32x4_t v[C::kVt ? 2 : C::K_CH];  // bf16: four 8-byte rows packed into two 16-byte registers
+  u32x4_t v[C::K_CH];
 
   __device__ __forceinline__ void load(const FwdParams& p, int kvh, int kv0, int tid) {
     const int64_t row_bytes = int64_t(p.hk) * D * C::E;
@@ -105,22 +88,7 @@ struct Tile {
       const int row = c / C::CPR, col = c % C::CPR;
       const int key = kv0 + row;
       k[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(kb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
-      if constexpr (!C::kVt)
-        v[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(vb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
-    }
-    if constexpr (C::kVt) {
-      if (tid < C::V_PAIRS) {
-        // keys 4kg..4kg+3, dims 4dc..4dc+3 (8 bytes per key)
-        const int kg = tid % (BN / 4), dc = tid / (BN / 4);
-        u32x2_t r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kv0 + 4 * kg + i;
-          r[i] = key < p.N ? *reinterpret_cast<const u32x2_t*>(vb + key * row_bytes + dc * 8) : u32x2_t{0, 0};
-        }
-        v[0] = u32x4_t{r[0][0], r[0][1], r[1][0], r[1][1]};
-        v[1] = u32x4_t{r[2][0], r[2][1], r[3][0], r[3][1]};
-      }
+      v[i] = key < p.N ? *reinterpret_cast<const u32x4_t*>(vb + key * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -130,22 +98,7 @@ struct Tile {
       const int c = tid + kThreads * i;
       const int row = c / C::CPR, col = c % C::CPR;
       *reinterpret_cast<u32x4_t*>(lk + row * C::K_STRIDE + col * 16) = k[i];
-      if constexpr (!C::kVt) *reinterpret_cast<u32x4_t*>(lv + row * C::V_STRIDE + col * 16) = v[i];
-    }
-    if constexpr (C::kVt) {
-      if (tid < C::V_PAIRS) {
-        // key i of the group: words (v[i/2][2(i%2)], v[i/2][2(i%2)+1]) hold dims (0,1) and (2,3).
-        const int kg = tid % (BN / 4), dc = tid / (BN / 4);
-        char* base = lv + vt_slot(kg) * C::E;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t w0 = v[0][j], w1 = v[0][2 + j], w2 = v[1][j], w3 = v[1][2 + j];
-          const u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-          const u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-          *reinterpret_cast<u32x2_t*>(base + (dc * 4 + 2 * j) * C::V_STRIDE) = lo;
-          *reinterpret_cast<u32x2_t*>(base + (dc * 4 + 2 * j + 1) * C::V_STRIDE) = hi;
-        }
-      }
+      *reinterpret_cast<u32x4_t*>(lv + row * C::V_STRIDE + col * 16) = v[i];
     }
   }
 };
@@ -284,13 +237,8 @@ void attn_fwd_kernel(FwdParams p) {
       for (int st = 0; st < C::PV; ++st) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          frag_t a;
-          if constexpr (C::kVt) {
-            a = load_frag<Tr>(lv + (db * 32 + l32) * C::V_STRIDE + (st * 16 + half * 8) * E);
-          } else {
-            const int key = (st >> 4) * 32 + acc_row(st & 15, half);
-            a = load_frag<Tr>(lv + key * C::V_STRIDE + (db * 32 + l32) * E);
-          }
+          const int key = (st >> 4) * 32 + acc_row(st & 15, half);
+          const frag_t a = load_frag<Tr>(lv + key * C::V_STRIDE + (db * 32 + l32) * E);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) acc_o[db][qb] = mfma(a, pf[qb][st], acc_o[db][qb]);
         }
