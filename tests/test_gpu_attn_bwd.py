@@ -100,6 +100,22 @@ def test_bwd_small_full(N, P, Hq, Hkv, D, dtype, lens):
     check_grads(cfg, got, oracle_attention(run))
 
 
+def test_bwd_many_documents_full():
+    """Dozens of short documents (and an empty one): the bf16 kernels then run
+    their blocks in an order sorted by work, which must still cover every block
+    exactly once."""
+    rng = np.random.default_rng(123)
+    lens, total = [0], 0
+    while total < 8192:
+        lens.append(int(rng.integers(1, 600)))
+        total += lens[-1]
+    lens[-1] -= total - 8192
+    cfg = syn.custom(8192, 8, 32, 8, 128, "bf16", seed=99)
+    run = Run(cfg, cu=syn.cu_from_lengths(lens))
+    got = run_fwd_bwd(run)
+    check_grads(cfg, got, oracle_attention(run))
+
+
 def test_bwd_c5_packed_documents_full():
     cfg = syn.CONFIGS["c5"]
     run = Run(cfg)
