@@ -20,7 +20,7 @@ namespace uly {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = 8;  // 16-byte chunks per thread
+constexpr int kItems = 32;  // 16-byte chunks per thread
 
 struct PermuteArgs {
   char* shard[ULY_MAX_P];
@@ -61,20 +61,84 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   if (first + kThreads * kItems <= n_chunks) {
     // whole block in range: all kItems loads in flight before the first store
     // (named registers; a guarded array here ends up staged through memory)
-    static_assert(kItems == 8, "the fast path names its eight chunks");
-    const chunk_t v0 = load(base), v1 = load(base + kThreads), v2 = load(base + 2 * kThreads),
-                  v3 = load(base + 3 * kThreads), v4 = load(base + 4 * kThreads), v5 = load(base + 5 * kThreads),
-                  v6 = load(base + 6 * kThreads), v7 = load(base + 7 * kThreads);
+    static_assert(kItems == 32, "the fast path names its 32 chunks");
+    const chunk_t v0 = load(base),
+                  v1 = load(base + 1 * kThreads),
+                  v2 = load(base + 2 * kThreads),
+                  v3 = load(base + 3 * kThreads),
+                  v4 = load(base + 4 * kThreads),
+                  v5 = load(base + 5 * kThreads),
+                  v6 = load(base + 6 * kThreads),
+                  v7 = load(base + 7 * kThreads),
+                  v8 = load(base + 8 * kThreads),
+                  v9 = load(base + 9 * kThreads),
+                  v10 = load(base + 10 * kThreads),
+                  v11 = load(base + 11 * kThreads),
+                  v12 = load(base + 12 * kThreads),
+                  v13 = load(base + 13 * kThreads),
+                  v14 = load(base + 14 * kThreads),
+                  v15 = load(base + 15 * kThreads),
+                  v16 = load(base + 16 * kThreads),
+                  v17 = load(base + 17 * kThreads),
+                  v18 = load(base + 18 * kThreads),
+                  v19 = load(base + 19 * kThreads),
+                  v20 = load(base + 20 * kThreads),
+                  v21 = load(base + 21 * kThreads),
+                  v22 = load(base + 22 * kThreads),
+                  v23 = load(base + 23 * kThreads),
+                  v24 = load(base + 24 * kThreads),
+                  v25 = load(base + 25 * kThreads),
+                  v26 = load(base + 26 * kThreads),
+                  v27 = load(base + 27 * kThreads),
+                  v28 = load(base + 28 * kThreads),
+                  v29 = load(base + 29 * kThreads),
+                  v30 = load(base + 30 * kThreads),
+                  v31 = load(base + 31 * kThreads);
     store(base, v0);
-    store(base + kThreads, v1);
+    store(base + 1 * kThreads, v1);
     store(base + 2 * kThreads, v2);
     store(base + 3 * kThreads, v3);
     store(base + 4 * kThreads, v4);
     store(base + 5 * kThreads, v5);
     store(base + 6 * kThreads, v6);
     store(base + 7 * kThreads, v7);
+    store(base + 8 * kThreads, v8);
+    store(base + 9 * kThreads, v9);
+    store(base + 10 * kThreads, v10);
+    store(base + 11 * kThreads, v11);
+    store(base + 12 * kThreads, v12);
+    store(base + 13 * kThreads, v13);
+    store(base + 14 * kThreads, v14);
+    store(base + 15 * kThreads, v15);
+    store(base + 16 * kThreads, v16);
+    store(base + 17 * kThreads, v17);
+    store(base + 18 * kThreads, v18);
+    store(base + 19 * kThreads, v19);
+    store(base + 20 * kThreads, v20);
+    store(base + 21 * kThreads, v21);
+    store(base + 22 * kThreads, v22);
+    store(base + 23 * kThreads, v23);
+    store(base + 24 * kThreads, v24);
+    store(base + 25 * kThreads, v25);
+    store(base + 26 * kThreads, v26);
+    store(base + 27 * kThreads, v27);
+    store(base + 28 * kThreads, v28);
+    store(base + 29 * kThreads, v29);
+    store(base + 30 * kThreads, v30);
+    store(base + 31 * kThreads, v31);
   } else {
-    for (uint32_t i = base; i < n_chunks; i += kThreads) store(i, load(i));
+    // the last, partial block: four loads in flight per step
+    for (uint32_t i = base; i < n_chunks; i += 4 * kThreads) {
+      const bool g1 = i + kThreads < n_chunks, g2 = i + 2 * kThreads < n_chunks, g3 = i + 3 * kThreads < n_chunks;
+      const chunk_t v0 = load(i);
+      const chunk_t v1 = g1 ? load(i + kThreads) : chunk_t{};
+      const chunk_t v2 = g2 ? load(i + 2 * kThreads) : chunk_t{};
+      const chunk_t v3 = g3 ? load(i + 3 * kThreads) : chunk_t{};
+      store(i, v0);
+      if (g1) store(i + kThreads, v1);
+      if (g2) store(i + 2 * kThreads, v2);
+      if (g3) store(i + 3 * kThreads, v3);
+    }
   }
 }
 
