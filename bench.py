@@ -130,6 +130,37 @@ def copy_calibration() -> int:
     return 0
 
 
+def fused_qkv_rates(uly, cfg, reps: int) -> dict:
+    """The fused-projection variants of the redistribution on this workload's
+    shapes: ulysses_pack_qkv from [T, Hq + 2*Hkv, D] shards into the group's
+    q/k/v, and ulysses_unpack_qkv back (one launch each instead of three).
+    Not part of the step: the workload's shards are separate tensors."""
+    import torch
+    dev, tdt = "cuda:0", torch.bfloat16
+    P, T, D, Hq, Hkv, g = cfg.P, cfg.T, cfg.D, cfg.Hq, cfg.Hkv, cfg.group
+    shards = [torch.empty((T, Hq + 2 * Hkv, D), dtype=tdt, device=dev).normal_() for _ in range(P)]
+    outs = [torch.empty((P * T, c, D), dtype=tdt, device=dev) for c in (cfg.hq, cfg.hk, cfg.hk)]
+    nbytes = 2 * P * T * (cfg.hq + 2 * cfg.hk) * D * 2   # read + write, each once
+    res = {}
+    for name, fn in (("pack_qkv", lambda: uly.ulysses_pack_qkv(shards, Hq, Hkv, g, *outs)),
+                     ("unpack_qkv", lambda: uly.ulysses_unpack_qkv(*outs, Hq, Hkv, g, shards))):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    res["bytes"] = nbytes
+    del shards, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def _doc_starts(N, cu):
     cuv = np.array([0, N]) if cu is None else np.asarray(cu, dtype=np.int64)
     tok = np.arange(N)
@@ -284,6 +315,7 @@ def main() -> int:
         "roofline": roofline,
         "calls": details,
     }
+    line["fused_qkv"] = fused_qkv_rates(uly, cfg, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cu, host, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -15,6 +15,8 @@
  *   attn_fwd         causal (optionally packed-document) GQA attention forward
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
+ *   ulysses_pack_qkv / ulysses_unpack_qkv
+ *                    the same for a fused QKV projection output, one launch
  *
  * Notation: P ranks; T tokens per rank; N = P*T; H heads in a shard tensor;
  * a head group g owns the hh = H/P contiguous heads [g*hh, (g+1)*hh).
@@ -99,6 +101,40 @@ uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int 
  */
 uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt,
                           int group, void* const* shards, hipStream_t stream);
+
+/*
+ * ulysses_pack_qkv -- ulysses_pack for the output of a fused QKV projection,
+ * in one launch ("Snowflake's Ulysses trick ...", second paragraph: the
+ * all-to-all follows each GPU's local QKV projections). The pages do not give
+ * the fused layout; here a shard token holds the Hq query heads, then the Hkv
+ * key heads, then the Hkv value heads, each D elements:
+ *
+ *   shards[j] : [T][Hq + 2*Hkv][D]   (query heads [0, Hq), key heads
+ *               [Hq, Hq+Hkv), value heads [Hq+Hkv, Hq+2*Hkv))
+ *   q_out[j*T + t][h][:] = shards[j][t][group*hq + h][:]             h < hq = Hq/P
+ *   k_out[j*T + t][h][:] = shards[j][t][Hq + group*hk + h][:]        h < hk = Hkv/P
+ *   v_out[j*T + t][h][:] = shards[j][t][Hq + Hkv + group*hk + h][:]
+ *
+ * q_out : device [P*T][hq][D]; k_out, v_out : device [P*T][hk][D] (written
+ * in full). P in [1, ULY_MAX_P]; T >= 1; Hq % P == 0 and Hkv % P == 0;
+ * D in {64, 128}; 0 <= group < P. Bit-exact; other preconditions and errors
+ * as ulysses_pack.
+ */
+uly_status ulysses_pack_qkv(const void* const* shards, int P, int64_t T, int Hq, int Hkv, int D,
+                            uly_dtype dt, int group, void* q_out, void* k_out, void* v_out,
+                            hipStream_t stream);
+
+/*
+ * ulysses_unpack_qkv -- the inverse of ulysses_pack_qkv, in one launch: the
+ * head-group gradients dq [P*T][hq][D], dk and dv [P*T][hk][D] go back into
+ * the fused [T][Hq + 2*Hkv][D] layout of each shard (the gradient of the
+ * fused projection output; the backward's mirror of the second all-to-all).
+ * Only the group's heads of each section are written; every other head is
+ * left untouched. Same preconditions as ulysses_pack_qkv; bit-exact.
+ */
+uly_status ulysses_unpack_qkv(const void* dq, const void* dk, const void* dv, int P, int64_t T, int Hq,
+                              int Hkv, int D, uly_dtype dt, int group, void* const* shards,
+                              hipStream_t stream);
 
 /*
  * attn_fwd -- exact softmax attention for one head group over the full

@@ -12,6 +12,10 @@ What it computes (plain numpy, fp64 for all floating point):
                           sequence for a subset of heads; "Ulysses Sequence
                           Parallelism ...", the "All-to-All Communication" step:
                           a second all-to-all reverses it)
+  pack_qkv_ref / unpack_qkv_ref
+                          the same redistributions for a fused QKV projection
+                          output (query, key, value heads of a token side by
+                          side), one packed tensor per section
   attn_ref                exact masked softmax attention per head and its
                           analytic gradients (the plain definition that tiled
                           attention reproduces; "Ulysses Sequence Parallelism
@@ -26,6 +30,8 @@ from .ref import (  # noqa: F401
     bf16_bits_to_f64,
     doc_tables,
     f32_bits_to_f64,
+    pack_qkv_ref,
     pack_ref,
+    unpack_qkv_ref,
     unpack_ref,
 )

@@ -125,6 +125,77 @@ def unpack_ref(packed: np.ndarray, shards, group: int, tokens=None):
     return [x.reshape(T, H, D) for x in out]
 
 
+def _qkv_sections(shards, Hq: int, Hkv: int, group: int):
+    P = len(shards)
+    if P < 1:
+        raise ValueError("need at least one shard")
+    T, H, D = shards[0].shape
+    for s in shards:
+        if s.shape != (T, H, D) or s.dtype != shards[0].dtype:
+            raise ValueError("shards must share shape and dtype")
+    if H != Hq + 2 * Hkv or Hq % P or Hkv % P:
+        raise ValueError("fused shards need Hq + 2*Hkv heads with Hq, Hkv divisible by P")
+    if not 0 <= group < P:
+        raise ValueError("group out of range")
+    hq, hk = Hq // P, Hkv // P
+    # (first head of the group's slice inside a shard token, heads in the slice)
+    return P, T, H, D, [(group * hq, hq), (Hq + group * hk, hk), (Hq + Hkv + group * hk, hk)]
+
+
+def pack_qkv_ref(shards, Hq: int, Hkv: int, group: int):
+    """The first redistribution applied to a fused QKV projection output (the
+    all-to-all follows each GPU's local QKV projections: "Snowflake's Ulysses
+    trick ...", second paragraph). Layout reading: a shard token holds the Hq
+    query heads, then the Hkv key heads, then the Hkv value heads. For the
+    section starting at head b with the group's slice of c heads:
+
+        out[n, h, d] = shard_j[t, b + h, d],  n = j*T + t, h < c,
+
+    with b = group*hq (queries), Hq + group*hk (keys), Hq + Hkv + group*hk
+    (values). shards: P arrays [T, Hq + 2*Hkv, D] of raw bits. Returns the
+    three packed arrays (q [N, hq, D], k and v [N, hk, D]).
+    """
+    P, T, H, D, sections = _qkv_sections(shards, Hq, Hkv, group)
+    flats = [s.reshape(-1) for s in shards]
+    outs = []
+    for b, c in sections:
+        o = np.arange(P * T * c * D, dtype=np.int64)
+        d = o % D
+        h = (o // D) % c
+        n = o // (c * D)
+        j, t = n // T, n % T
+        src = (t * H + b + h) * D + d
+        out = np.empty(o.size, dtype=shards[0].dtype)
+        for jj in range(P):
+            sel = j == jj
+            out[sel] = flats[jj][src[sel]]
+        outs.append(out.reshape(P * T, c, D))
+    return tuple(outs)
+
+
+def unpack_qkv_ref(dq: np.ndarray, dk: np.ndarray, dv: np.ndarray, shards, Hq: int, Hkv: int, group: int):
+    """Inverse of pack_qkv_ref (the backward's mirror of the second
+    redistribution): shard_j[t, b + h, d] = packed[j*T + t, h, d] for the
+    three sections; heads outside the group's slices keep the values in
+    `shards`, which is not modified (new arrays are returned)."""
+    P, T, H, D, sections = _qkv_sections(shards, Hq, Hkv, group)
+    out = [s.copy().reshape(-1) for s in shards]
+    for packed, (b, c) in zip((dq, dk, dv), sections):
+        if packed.shape != (P * T, c, D):
+            raise ValueError("packed shape mismatch")
+        o = np.arange(P * T * c * D, dtype=np.int64)
+        d = o % D
+        h = (o // D) % c
+        n = o // (c * D)
+        j, t = n // T, n % T
+        dst = (t * H + b + h) * D + d
+        flat_in = packed.reshape(-1)
+        for jj in range(P):
+            sel = j == jj
+            out[jj][dst[sel]] = flat_in[o[sel]]
+    return [x.reshape(T, H, D) for x in out]
+
+
 # ---------------------------------------------------------------------------
 # documents
 # ---------------------------------------------------------------------------

@@ -26,6 +26,10 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "ulysses_pack": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
+    "ulysses_pack_qkv": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                 _vp]),
+    "ulysses_unpack_qkv": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32,
+                                   ctypes.POINTER(_vp), _vp]),
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32, _f32, _i32, _vp]),
     "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
@@ -140,6 +144,42 @@ def ulysses_unpack(inp, group: int, shards: Sequence, stream=None) -> None:
         _dev(inp, (P * T, H // P, D), dt, "inp")
     _raise(lib().ulysses_unpack(ctypes.c_void_p(inp.data_ptr()), P, T, H, D, _dtype_code(shards[0]), group,
                                 ptrs, _stream(stream)))
+
+
+def _qkv_shards(shards, Hq: int, Hkv: int):
+    P = len(shards)
+    T, H, D = shards[0].shape
+    if H != Hq + 2 * Hkv:
+        raise ValueError(f"fused shards have {H} heads, expected Hq + 2*Hkv = {Hq + 2 * Hkv}")
+    dt = shards[0].dtype
+    ptrs = (ctypes.c_void_p * P)(*[_dev(s, (T, H, D), dt, f"shards[{j}]").value for j, s in enumerate(shards)])
+    return P, T, D, dt, ptrs
+
+
+def ulysses_pack_qkv(shards: Sequence, Hq: int, Hkv: int, group: int, q_out, k_out, v_out, stream=None) -> None:
+    """Fused-QKV pack: shards[j] is [T, Hq + 2*Hkv, D] (query, then key, then
+    value heads); writes the group's q/k/v heads of every token (see
+    include/ulysses.h)."""
+    P, T, D, dt, ptrs = _qkv_shards(shards, Hq, Hkv)
+    if Hq % P == 0 and Hkv % P == 0:
+        _dev(q_out, (P * T, Hq // P, D), dt, "q_out")
+        _dev(k_out, (P * T, Hkv // P, D), dt, "k_out")
+        _dev(v_out, (P * T, Hkv // P, D), dt, "v_out")
+    _raise(lib().ulysses_pack_qkv(ptrs, P, T, Hq, Hkv, D, _dtype_code(shards[0]), group,
+                                  ctypes.c_void_p(q_out.data_ptr()), ctypes.c_void_p(k_out.data_ptr()),
+                                  ctypes.c_void_p(v_out.data_ptr()), _stream(stream)))
+
+
+def ulysses_unpack_qkv(dq, dk, dv, Hq: int, Hkv: int, group: int, shards: Sequence, stream=None) -> None:
+    """Inverse of ulysses_pack_qkv; heads outside the group are untouched."""
+    P, T, D, dt, ptrs = _qkv_shards(shards, Hq, Hkv)
+    if Hq % P == 0 and Hkv % P == 0:
+        _dev(dq, (P * T, Hq // P, D), dt, "dq")
+        _dev(dk, (P * T, Hkv // P, D), dt, "dk")
+        _dev(dv, (P * T, Hkv // P, D), dt, "dv")
+    _raise(lib().ulysses_unpack_qkv(ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()),
+                                    ctypes.c_void_p(dv.data_ptr()), P, T, Hq, Hkv, D, _dtype_code(shards[0]),
+                                    group, ptrs, _stream(stream)))
 
 
 def attn_fwd(q, k, v, o, lse, softmax_scale: float, cu_seqlens=None, causal: int = 1, stream=None) -> None:

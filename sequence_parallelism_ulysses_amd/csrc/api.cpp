@@ -51,10 +51,39 @@ uly_status check_permute(const char* fn, int P, int64_t T, int H, int D, int dt,
   out->P = P;
   out->T = T;
   out->row_bytes = H * D * e;
-  out->seg_bytes = hh * D * e;
-  out->head_offset = group * hh * D * e;
-  CHECK(T * (out->seg_bytes / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
-        "%s: one shard's head group (%lld bytes) exceeds 32 GiB", fn, (long long)(T * out->seg_bytes));
+  out->nseg = 1;
+  out->seg_bytes[0] = hh * D * e;
+  out->head_offset[0] = group * hh * D * e;
+  CHECK(T * (out->seg_bytes[0] / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
+        "%s: one shard's head group (%lld bytes) exceeds 32 GiB", fn, (long long)(T * out->seg_bytes[0]));
+  return ULY_OK;
+}
+
+// A fused QKV shard token holds Hq query heads, then Hkv key heads, then Hkv
+// value heads; the group's slice of each section is one segment.
+uly_status check_permute_qkv(const char* fn, int P, int64_t T, int Hq, int Hkv, int D, int dt, int group,
+                             uly::PermuteDesc* out) {
+  CHECK(P >= 1 && P <= ULY_MAX_P, ULY_ERR_INVALID_ARG, "%s: P=%d must be in [1, %d]", fn, P, ULY_MAX_P);
+  CHECK(T >= 1, ULY_ERR_INVALID_ARG, "%s: T=%lld must be >= 1", fn, (long long)T);
+  CHECK(Hq >= 1 && Hq % P == 0, ULY_ERR_INVALID_ARG, "%s: Hq=%d must be a positive multiple of P=%d", fn, Hq, P);
+  CHECK(Hkv >= 1 && Hkv % P == 0, ULY_ERR_INVALID_ARG, "%s: Hkv=%d must be a positive multiple of P=%d", fn, Hkv, P);
+  CHECK(Hq <= (1 << 20) && Hkv <= (1 << 20), ULY_ERR_INVALID_ARG, "%s: Hq=%d, Hkv=%d too large", fn, Hq, Hkv);
+  CHECK(D == 64 || D == 128, ULY_ERR_INVALID_ARG, "%s: D=%d must be 64 or 128", fn, D);
+  CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
+  CHECK(group >= 0 && group < P, ULY_ERR_INVALID_ARG, "%s: group=%d must be in [0, P=%d)", fn, group, P);
+  const int64_t e = elem_bytes(static_cast<uly_dtype>(dt));
+  const int64_t hq = Hq / P, hk = Hkv / P;
+  out->P = P;
+  out->T = T;
+  out->row_bytes = int64_t(Hq + 2 * Hkv) * D * e;
+  out->nseg = 3;
+  out->seg_bytes[0] = hq * D * e;
+  out->seg_bytes[1] = out->seg_bytes[2] = hk * D * e;
+  out->head_offset[0] = group * hq * D * e;
+  out->head_offset[1] = (int64_t(Hq) + group * hk) * D * e;
+  out->head_offset[2] = (int64_t(Hq) + Hkv + group * hk) * D * e;
+  CHECK(T * (out->seg_bytes[0] / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
+        "%s: one shard's query head group (%lld bytes) exceeds 32 GiB", fn, (long long)(T * out->seg_bytes[0]));
   return ULY_OK;
 }
 
@@ -111,7 +140,8 @@ uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int 
   for (int j = 0; j < P; ++j)
     CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
           "ulysses_pack: shards[%d] is NULL or not 16-byte aligned", j);
-  return from_hip(uly::launch_pack(shards, out, d, stream), "ulysses_pack");
+  void* const outs[1] = {out};
+  return from_hip(uly::launch_pack(shards, outs, d, stream), "ulysses_pack");
 }
 
 uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt, int group,
@@ -124,7 +154,44 @@ uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dt
   for (int j = 0; j < P; ++j)
     CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
           "ulysses_unpack: shards[%d] is NULL or not 16-byte aligned", j);
-  return from_hip(uly::launch_unpack(in, shards, d, stream), "ulysses_unpack");
+  const void* const ins[1] = {in};
+  return from_hip(uly::launch_unpack(ins, shards, d, stream), "ulysses_unpack");
+}
+
+uly_status ulysses_pack_qkv(const void* const* shards, int P, int64_t T, int Hq, int Hkv, int D,
+                            uly_dtype dt, int group, void* q_out, void* k_out, void* v_out,
+                            hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_permute_qkv("ulysses_pack_qkv", P, T, Hq, Hkv, D, dt, group, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr, ULY_ERR_INVALID_ARG, "ulysses_pack_qkv: shards is NULL");
+  void* const outs[3] = {q_out, k_out, v_out};
+  const char* names[3] = {"q_out", "k_out", "v_out"};
+  for (int i = 0; i < 3; ++i)
+    CHECK(outs[i] != nullptr && aligned16(outs[i]), ULY_ERR_INVALID_ARG,
+          "ulysses_pack_qkv: %s is NULL or not 16-byte aligned", names[i]);
+  for (int j = 0; j < P; ++j)
+    CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
+          "ulysses_pack_qkv: shards[%d] is NULL or not 16-byte aligned", j);
+  return from_hip(uly::launch_pack(shards, outs, d, stream), "ulysses_pack_qkv");
+}
+
+uly_status ulysses_unpack_qkv(const void* dq, const void* dk, const void* dv, int P, int64_t T, int Hq,
+                              int Hkv, int D, uly_dtype dt, int group, void* const* shards,
+                              hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_permute_qkv("ulysses_unpack_qkv", P, T, Hq, Hkv, D, dt, group, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr, ULY_ERR_INVALID_ARG, "ulysses_unpack_qkv: shards is NULL");
+  const void* const ins[3] = {dq, dk, dv};
+  const char* names[3] = {"dq", "dk", "dv"};
+  for (int i = 0; i < 3; ++i)
+    CHECK(ins[i] != nullptr && aligned16(ins[i]), ULY_ERR_INVALID_ARG,
+          "ulysses_unpack_qkv: %s is NULL or not 16-byte aligned", names[i]);
+  for (int j = 0; j < P; ++j)
+    CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
+          "ulysses_unpack_qkv: shards[%d] is NULL or not 16-byte aligned", j);
+  return from_hip(uly::launch_unpack(ins, shards, d, stream), "ulysses_unpack_qkv");
 }
 
 uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N,

@@ -10,18 +10,24 @@
 
 namespace uly {
 
-// Byte-level description of one pack/unpack call.
+#define ULY_PERMUTE_MAX_SEGMENTS 3
+
+// Byte-level description of one pack/unpack call: nseg segments of every
+// shard token (one for a single tensor; Q, K, V for a fused QKV tensor), each
+// moved to or from its own packed tensor.
 struct PermuteDesc {
   int P;
   int64_t T;             // tokens per shard
-  int64_t row_bytes;     // H * D * elem   (one token of a shard)
-  int64_t seg_bytes;     // hh * D * elem  (one token of the head group)
-  int64_t head_offset;   // group * hh * D * elem
+  int64_t row_bytes;     // bytes of one shard token (all its heads)
+  int nseg;              // 1 .. ULY_PERMUTE_MAX_SEGMENTS
+  int64_t seg_bytes[ULY_PERMUTE_MAX_SEGMENTS];    // hh * D * elem of segment s
+  int64_t head_offset[ULY_PERMUTE_MAX_SEGMENTS];  // byte offset of segment s in a shard token
 };
 
-hipError_t launch_pack(const void* const* shards, void* out, const PermuteDesc& d,
+// out / in: nseg packed tensors, one per segment.
+hipError_t launch_pack(const void* const* shards, void* const* out, const PermuteDesc& d,
                        hipStream_t stream);
-hipError_t launch_unpack(const void* in, void* const* shards, const PermuteDesc& d,
+hipError_t launch_unpack(const void* const* in, void* const* shards, const PermuteDesc& d,
                          hipStream_t stream);
 
 struct AttnDesc {

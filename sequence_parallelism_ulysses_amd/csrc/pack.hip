@@ -14,6 +14,11 @@
 // before it stores, consecutive lanes touch consecutive chunks (full 64-byte
 // lines per 4 lanes), loads and stores are non-temporal, and one grid row per
 // shard keeps the shard pointer uniform across the workgroup.
+//
+// One launch can move up to three segments of each shard token (the Q, K and
+// V heads of a fused QKV projection output, each into its own packed tensor):
+// the grid's x range is split into consecutive block ranges, one per
+// segment, so every workgroup copies chunks of a single segment.
 #include "internal.hpp"
 
 namespace uly {
@@ -21,15 +26,22 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kItems = 32;  // 16-byte chunks per thread
+constexpr int kMaxSegments = 3;
+
+struct Segment {
+  char* packed;             // [P*T][seg_bytes] packed tensor of this segment
+  uint64_t seg_bytes;       // bytes of one token's segment
+  uint64_t head_offset;     // byte offset of the segment inside a shard token
+  uint32_t chunks_per_row;  // seg_bytes / 16
+  uint32_t block_begin;     // first blockIdx.x of this segment
+};
 
 struct PermuteArgs {
   char* shard[ULY_MAX_P];
-  char* packed;
+  Segment seg[kMaxSegments];
+  uint32_t nseg;
   uint32_t T;               // tokens per shard
-  uint32_t chunks_per_row;  // seg_bytes / 16
-  uint64_t row_bytes;
-  uint64_t seg_bytes;
-  uint64_t head_offset;
+  uint64_t row_bytes;       // bytes of one shard token
 };
 
 typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte chunk
@@ -37,16 +49,20 @@ typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte ch
 template <bool kPack>
 __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   const uint32_t j = blockIdx.y;
-  const uint32_t n_chunks = a.T * a.chunks_per_row;  // < 2^31, checked on the host
+  // the segment of this workgroup (wave-uniform selects, no indexed kernarg)
+  Segment sg = a.seg[0];
+  if (a.nseg > 1 && blockIdx.x >= a.seg[1].block_begin) sg = a.seg[1];
+  if (a.nseg > 2 && blockIdx.x >= a.seg[2].block_begin) sg = a.seg[2];
+  const uint32_t n_chunks = a.T * sg.chunks_per_row;  // < 2^31, checked on the host
   char* shard = a.shard[j];
-  char* packed = a.packed + (uint64_t)j * a.T * a.seg_bytes;
-  const uint32_t first = blockIdx.x * (kThreads * kItems);
+  char* packed = sg.packed + (uint64_t)j * a.T * sg.seg_bytes;
+  const uint32_t first = (blockIdx.x - sg.block_begin) * (kThreads * kItems);
   const uint32_t base = first + threadIdx.x;
 
   auto shard_off = [&](uint32_t i) {
-    const uint32_t t = i / a.chunks_per_row;
-    const uint32_t c = i - t * a.chunks_per_row;
-    return (uint64_t)t * a.row_bytes + a.head_offset + 16ull * c;
+    const uint32_t t = i / sg.chunks_per_row;
+    const uint32_t c = i - t * sg.chunks_per_row;
+    return (uint64_t)t * a.row_bytes + sg.head_offset + 16ull * c;
   };
   // Every byte is touched once: non-temporal loads and stores keep the
   // stream from displacing cache lines that other work still needs (and on
@@ -142,40 +158,53 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   }
 }
 
-PermuteArgs make_args(const PermuteDesc& d) {
-  PermuteArgs a{};
-  a.T = static_cast<uint32_t>(d.T);
-  a.chunks_per_row = static_cast<uint32_t>(d.seg_bytes / 16);
-  a.row_bytes = d.row_bytes;
-  a.seg_bytes = d.seg_bytes;
-  a.head_offset = d.head_offset;
-  return a;
+uint32_t blocks_for(int64_t T, int64_t seg_bytes) {
+  const uint64_t n_chunks = static_cast<uint64_t>(T) * static_cast<uint64_t>(seg_bytes / 16);
+  const uint64_t per_block = kThreads * kItems;
+  return static_cast<uint32_t>((n_chunks + per_block - 1) / per_block);
 }
 
-dim3 grid_for(const PermuteDesc& d) {
-  const uint64_t n_chunks = static_cast<uint64_t>(d.T) * (d.seg_bytes / 16);
-  const uint64_t per_block = kThreads * kItems;
-  return dim3(static_cast<unsigned>((n_chunks + per_block - 1) / per_block),
-              static_cast<unsigned>(d.P), 1);
+// Fill the launch arguments for the segments of `d`, with `packed[s]` the
+// packed tensor of segment s; returns the grid (x over segments, y over shards).
+dim3 make_args(const PermuteDesc& d, char* const* packed, PermuteArgs& a) {
+  a = PermuteArgs{};
+  a.T = static_cast<uint32_t>(d.T);
+  a.row_bytes = static_cast<uint64_t>(d.row_bytes);
+  a.nseg = static_cast<uint32_t>(d.nseg);
+  uint32_t blocks = 0;
+  for (int s = 0; s < d.nseg; ++s) {
+    a.seg[s].packed = packed[s];
+    a.seg[s].seg_bytes = static_cast<uint64_t>(d.seg_bytes[s]);
+    a.seg[s].head_offset = static_cast<uint64_t>(d.head_offset[s]);
+    a.seg[s].chunks_per_row = static_cast<uint32_t>(d.seg_bytes[s] / 16);
+    a.seg[s].block_begin = blocks;
+    blocks += blocks_for(d.T, d.seg_bytes[s]);
+  }
+  return dim3(blocks, static_cast<unsigned>(d.P), 1);
 }
 
 }  // namespace
 
-hipError_t launch_pack(const void* const* shards, void* out, const PermuteDesc& d,
+hipError_t launch_pack(const void* const* shards, void* const* out, const PermuteDesc& d,
                        hipStream_t stream) {
-  PermuteArgs a = make_args(d);
+  static_assert(kMaxSegments == ULY_PERMUTE_MAX_SEGMENTS, "segment count");
+  PermuteArgs a;
+  char* packed[kMaxSegments] = {};
+  for (int s = 0; s < d.nseg; ++s) packed[s] = static_cast<char*>(out[s]);
+  const dim3 grid = make_args(d, packed, a);
   for (int j = 0; j < d.P; ++j) a.shard[j] = const_cast<char*>(static_cast<const char*>(shards[j]));
-  a.packed = static_cast<char*>(out);
-  permute_kernel<true><<<grid_for(d), kThreads, 0, stream>>>(a);
+  permute_kernel<true><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(const void* in, void* const* shards, const PermuteDesc& d,
+hipError_t launch_unpack(const void* const* in, void* const* shards, const PermuteDesc& d,
                          hipStream_t stream) {
-  PermuteArgs a = make_args(d);
+  PermuteArgs a;
+  char* packed[kMaxSegments] = {};
+  for (int s = 0; s < d.nseg; ++s) packed[s] = const_cast<char*>(static_cast<const char*>(in[s]));
+  const dim3 grid = make_args(d, packed, a);
   for (int j = 0; j < d.P; ++j) a.shard[j] = static_cast<char*>(shards[j]);
-  a.packed = const_cast<char*>(static_cast<const char*>(in));
-  permute_kernel<false><<<grid_for(d), kThreads, 0, stream>>>(a);
+  permute_kernel<false><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "uly_check_cu_seqlens", "uly_last_error",
-        "ulysses_pack", "ulysses_unpack"])
+        "ulysses_pack", "ulysses_pack_qkv", "ulysses_unpack", "ulysses_unpack_qkv"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -81,6 +81,50 @@ def test_pack_rejects(kw, status, needle):
 ])
 def test_unpack_rejects(kw, needle):
     assert _unpack(**kw) == uly.ULY_ERR_INVALID_ARG
+    assert needle in uly.last_error()
+
+
+def _pack_qkv(**kw):
+    a = dict(shards=_ptrs(8), P=8, T=4096, Hq=32, Hkv=8, D=128, dt=uly.ULY_BF16, group=0,
+             q=FAKE, k=FAKE + 4096, v=FAKE + 8192, stream=None)
+    a.update(kw)
+    return uly.lib().ulysses_pack_qkv(a["shards"], a["P"], a["T"], a["Hq"], a["Hkv"], a["D"], a["dt"], a["group"],
+                                      a["q"], a["k"], a["v"], a["stream"])
+
+
+def _unpack_qkv(**kw):
+    a = dict(dq=FAKE, dk=FAKE + 4096, dv=FAKE + 8192, P=8, T=4096, Hq=32, Hkv=8, D=128, dt=uly.ULY_BF16,
+             group=0, shards=_ptrs(8), stream=None)
+    a.update(kw)
+    return uly.lib().ulysses_unpack_qkv(a["dq"], a["dk"], a["dv"], a["P"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                        a["dt"], a["group"], a["shards"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(P=0, shards=_ptrs(1)), uly.ULY_ERR_INVALID_ARG, "P=0"),
+    (dict(T=0), uly.ULY_ERR_INVALID_ARG, "T=0"),
+    (dict(Hq=30), uly.ULY_ERR_INVALID_ARG, "Hq=30"),
+    (dict(Hkv=4), uly.ULY_ERR_INVALID_ARG, "Hkv=4"),
+    (dict(Hkv=0), uly.ULY_ERR_INVALID_ARG, "Hkv=0"),
+    (dict(D=32), uly.ULY_ERR_INVALID_ARG, "D=32"),
+    (dict(dt=5), uly.ULY_ERR_INVALID_ARG, "dtype"),
+    (dict(group=8), uly.ULY_ERR_INVALID_ARG, "group=8"),
+    (dict(k=None), uly.ULY_ERR_INVALID_ARG, "k_out"),
+    (dict(v=FAKE + 8), uly.ULY_ERR_INVALID_ARG, "v_out"),
+    (dict(shards=(ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))), uly.ULY_ERR_INVALID_ARG, "shards[7]"),
+    (dict(T=1 << 26, Hq=64, Hkv=8, P=1, shards=_ptrs(1)), uly.ULY_ERR_UNSUPPORTED, "32 GiB"),
+])
+def test_pack_qkv_rejects(kw, status, needle):
+    assert _pack_qkv(**kw) == status
+    assert needle in uly.last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(dq=None), "dq is NULL"), (dict(dv=FAKE + 4), "dv is NULL"), (dict(Hkv=12), "Hkv=12"),
+    (dict(shards=None), "shards is NULL"),
+])
+def test_unpack_qkv_rejects(kw, needle):
+    assert _unpack_qkv(**kw) == uly.ULY_ERR_INVALID_ARG
     assert needle in uly.last_error()
 
 

@@ -5,7 +5,7 @@ import torch
 
 import sequence_parallelism_ulysses_amd as uly
 import synthetic as syn
-from oracle import pack_ref, unpack_ref
+from oracle import pack_qkv_ref, pack_ref, unpack_qkv_ref, unpack_ref
 from harness import DEV, bits_to_dev, dev_to_bits
 
 pytestmark = pytest.mark.gpu
@@ -116,3 +116,66 @@ def test_pack_rejects_mismatched_tensors():
         uly.ulysses_pack(dev, 0, torch.zeros((32, 3, 64), dtype=torch.bfloat16, device=DEV))
     with pytest.raises(uly.UlyssesError):
         uly.ulysses_pack(dev, 4, torch.zeros((32, 2, 64), dtype=torch.bfloat16, device=DEV))
+
+
+QKV_CASES = [
+    # (P, T, Hq, Hkv, D, dtype)
+    (8, 4096, 32, 8, 128, "bf16"),   # Llama-3.1-8B-shaped fused projection, 32k tokens over 8 ranks
+    (4, 256, 8, 8, 64, "f32"),       # the tiny fp32 shapes
+    (3, 37, 6, 3, 64, "bf16"),       # ragged: odd T, one kv head per group
+    (1, 5, 4, 2, 128, "bf16"),       # one rank
+    (2, 3000, 16, 4, 128, "bf16"),   # a partial last block in every section
+    (64, 2, 64, 64, 64, "bf16"),     # the largest rank count
+]
+
+
+@pytest.mark.parametrize("P,T,Hq,Hkv,D,dtype", QKV_CASES)
+def test_pack_unpack_qkv_bit_exact(P, T, Hq, Hkv, D, dtype):
+    """Fused QKV pack and its inverse against the oracle, bit for bit, with
+    random bit patterns; the inverse writes into canary-filled shards."""
+    H = Hq + 2 * Hkv
+    host = _host_shards(P, T, H, D, dtype, seed=7 * P + T)
+    dev = [bits_to_dev(s) for s in host]
+    tdt = dev[0].dtype
+    hq, hk = Hq // P, Hkv // P
+    for g in sorted({0, P - 1, P // 2}):
+        outs = [torch.empty((P * T, c, D), dtype=tdt, device=DEV) for c in (hq, hk, hk)]
+        uly.ulysses_pack_qkv(dev, Hq, Hkv, g, *outs)
+        torch.cuda.synchronize()
+        want = pack_qkv_ref(host, Hq, Hkv, g)
+        for name, o, w in zip("qkv", outs, want):
+            assert np.array_equal(dev_to_bits(o), w), f"pack_qkv {name} group {g}"
+        canary_bits = np.full((T, H, D), 0x7FA5 if dtype == "bf16" else 0x7FC0A5A5, dtype=host[0].dtype)
+        canary = [bits_to_dev(canary_bits.copy()) for _ in range(P)]
+        uly.ulysses_unpack_qkv(*outs, Hq, Hkv, g, canary)
+        torch.cuda.synchronize()
+        want_sh = unpack_qkv_ref(*want, [canary_bits] * P, Hq, Hkv, g)
+        for j in range(P):
+            assert np.array_equal(dev_to_bits(canary[j]), want_sh[j]), f"unpack_qkv group {g} shard {j}"
+
+
+def test_pack_qkv_equals_separate_packs():
+    """The fused call and three ulysses_pack calls on the sections (strided
+    views copied out) give the same bits (Llama-3.1-8B shapes, 128k tokens)."""
+    P, T, Hq, Hkv, D = 8, 16384, 32, 8, 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    dev = [torch.randint(-32768, 32767, (T, Hq + 2 * Hkv, D), dtype=torch.int16, device=DEV, generator=gen)
+           .view(torch.bfloat16) for _ in range(P)]
+    g = 3
+    fused = [torch.empty((P * T, c, D), dtype=torch.bfloat16, device=DEV) for c in (4, 1, 1)]
+    uly.ulysses_pack_qkv(dev, Hq, Hkv, g, *fused)
+    bounds = [(0, Hq), (Hq, Hq + Hkv), (Hq + Hkv, Hq + 2 * Hkv)]
+    for (a, b), f in zip(bounds, fused):
+        sec = [s[:, a:b].contiguous() for s in dev]
+        sep = torch.empty_like(f)
+        uly.ulysses_pack(sec, g, sep)
+        torch.cuda.synchronize()
+        assert torch.equal(sep.view(torch.int16), f.view(torch.int16))
+    # the oracle on sampled tokens of every shard (first, last, block edges)
+    ts = np.array([0, 1, 8191, 8192, T - 2, T - 1])
+    mini = [dev_to_bits(s[torch.from_numpy(ts).to(DEV)]) for s in dev]
+    want = pack_qkv_ref(mini, Hq, Hkv, g)
+    rows = torch.from_numpy(np.concatenate([j * T + ts for j in range(P)])).to(DEV)
+    for f, w in zip(fused, want):
+        assert np.array_equal(dev_to_bits(f[rows]), w)

@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_ref, bf16_bits_to_f64, doc_tables, f32_bits_to_f64, pack_ref, unpack_ref
+from oracle import (attn_ref, bf16_bits_to_f64, doc_tables, f32_bits_to_f64, pack_qkv_ref, pack_ref,
+                    unpack_qkv_ref, unpack_ref)
 from synthetic import cu_from_lengths
 
 
@@ -110,6 +111,76 @@ def test_pack_token_subset():
         for t in range(T):
             if (j, t) not in written:
                 assert not a[j][t].any()
+
+
+# ------------------------------------------------------- fused QKV pack/unpack
+@pytest.mark.parametrize("P,T,Hq,Hkv,D,g", [(2, 3, 4, 2, 2, 1), (4, 2, 8, 4, 3, 3), (1, 4, 3, 1, 2, 0),
+                                            (2, 2, 2, 2, 1, 0)])
+def test_pack_qkv_matches_python_loops(P, T, Hq, Hkv, D, g):
+    """Brute force over (shard, token, head, dim) with the section offsets
+    written out. Catches a wrong section base (keys read from the query
+    section, values from the keys) or a group offset scaled by the wrong head
+    count."""
+    H = Hq + 2 * Hkv
+    sh = _shards(P, T, H, D, seed=21)
+    hq, hk = Hq // P, Hkv // P
+    want = [np.zeros((P * T, c, D), np.uint16) for c in (hq, hk, hk)]
+    for j in range(P):
+        for t in range(T):
+            for d in range(D):
+                for h in range(hq):
+                    want[0][j * T + t, h, d] = sh[j][t, g * hq + h, d]
+                for h in range(hk):
+                    want[1][j * T + t, h, d] = sh[j][t, Hq + g * hk + h, d]
+                    want[2][j * T + t, h, d] = sh[j][t, Hq + Hkv + g * hk + h, d]
+    got = pack_qkv_ref(sh, Hq, Hkv, g)
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("P,T,Hq,Hkv,D", [(8, 3, 32, 8, 4), (4, 5, 4, 4, 2), (2, 1, 6, 2, 1)])
+def test_pack_qkv_equals_split_and_slice(P, T, Hq, Hkv, D):
+    """Closed form with library ops: split the fused heads into the query,
+    key and value sections (numpy split), concatenate shards along tokens,
+    slice each section's group heads."""
+    sh = _shards(P, T, Hq + 2 * Hkv, D, dtype=np.uint32, seed=23)
+    full = np.concatenate(sh, axis=0)
+    qs, ks, vs = np.split(full, [Hq, Hq + Hkv], axis=1)
+    hq, hk = Hq // P, Hkv // P
+    for g in range(P):
+        q, k, v = pack_qkv_ref(sh, Hq, Hkv, g)
+        assert np.array_equal(q, qs[:, g * hq:(g + 1) * hq])
+        assert np.array_equal(k, ks[:, g * hk:(g + 1) * hk])
+        assert np.array_equal(v, vs[:, g * hk:(g + 1) * hk])
+
+
+def test_unpack_qkv_inverts_pack_qkv_and_leaves_other_heads():
+    """unpack_qkv(pack_qkv(X, g), g) rebuilds X from a copy whose group slices
+    were zeroed; canaries in every other head survive; unpacking every group
+    into zeros rebuilds X (the groups' slices tile the fused heads)."""
+    P, T, Hq, Hkv, D = 4, 5, 8, 4, 3
+    H = Hq + 2 * Hkv
+    sh = _shards(P, T, H, D, seed=25)
+    hq, hk = Hq // P, Hkv // P
+    cur = [np.zeros_like(s) for s in sh]
+    for g in range(P):
+        packed = pack_qkv_ref(sh, Hq, Hkv, g)
+        mine = np.zeros(H, bool)
+        mine[g * hq:(g + 1) * hq] = True
+        mine[Hq + g * hk:Hq + (g + 1) * hk] = True
+        mine[Hq + Hkv + g * hk:Hq + Hkv + (g + 1) * hk] = True
+        holed = [s.copy() for s in sh]
+        for s in holed:
+            s[:, mine, :] = 0
+        for a, b in zip(unpack_qkv_ref(*packed, holed, Hq, Hkv, g), sh):
+            assert np.array_equal(a, b)
+        canary = [np.full_like(s, 0xBEEF) for s in sh]
+        for o, s in zip(unpack_qkv_ref(*packed, canary, Hq, Hkv, g), sh):
+            assert np.all(o[:, ~mine, :] == 0xBEEF)
+            assert np.array_equal(o[:, mine, :], s[:, mine, :])
+        cur = unpack_qkv_ref(*packed, cur, Hq, Hkv, g)
+    for a, b in zip(cur, sh):
+        assert np.array_equal(a, b)
 
 
 def test_bits_decoding():
