@@ -12,7 +12,8 @@
  * library implements the per-GPU pieces of that path:
  *
  *   ulysses_pack     sequence-sharded -> head-sharded layout for one head group
- *   attn_fwd         causal (optionally packed-document) GQA attention forward
+ *   attn_fwd         causal or document-masked (optionally packed-document) GQA
+ *                    attention forward
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
  *   ulysses_pack_qkv / ulysses_unpack_qkv
@@ -143,7 +144,7 @@ uly_status ulysses_unpack_qkv(const void* dq, const void* dk, const void* dv, in
  * attention keeps memory linear while computing the same result).
  *
  * For local q head h (kv head h/G), query i and key j, with the mask
- * M_ij = (j <= i) and doc(j) == doc(i):
+ * M_ij = (j <= i or causal == 0) and doc(j) == doc(i):
  *   S_ij = softmax_scale * q_i . k_j              (masked: -inf)
  *   lse_i = log sum_j exp(S_ij)                   (natural log)
  *   o_i  = sum_j exp(S_ij - lse_i) v_j
@@ -154,9 +155,14 @@ uly_status ulysses_unpack_qkv(const void* dq, const void* dk, const void* dv, in
  *            documents allowed), or NULL for one document of N tokens. Its
  *            contents are a precondition, not checked here (see
  *            uly_check_cu_seqlens); ndocs is ignored when it is NULL.
+ * causal : 1 for the causal mask the configurations use (the pages train
+ *          causal language models); 0 drops the j <= i bound, so every token
+ *          sees its whole document (the pages do not say; offered because
+ *          a key/value chunk that lies entirely before a query chunk, as in
+ *          chunked or ring-style attention, is seen this way).
  * N >= 1; hq % hk == 0; D in {64, 128}; softmax_scale finite and > 0;
- * causal must be 1 (non-causal returns ULY_ERR_UNSUPPORTED).
- * ULY_F32 requires D == 64 or 128 and runs in float32 throughout.
+ * causal in {0, 1}. ULY_F32 requires D == 64 or 128 and runs in float32
+ * throughout.
  */
 uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                     int64_t N, int hq, int hk, int D, uly_dtype dt,
@@ -188,7 +194,8 @@ uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype d
  * dq, dk, dv are overwritten (dk/dv hold the sum over the G q heads of each
  * kv head). workspace: device memory of at least attn_bwd_workspace_size()
  * bytes, 16-byte aligned, owned by the caller, contents ignored.
- * Other preconditions as attn_fwd. Results are deterministic (no atomics).
+ * causal must match the attn_fwd call that produced o and lse. Other
+ * preconditions as attn_fwd. Results are deterministic (no atomics).
  */
 uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,

@@ -96,7 +96,6 @@ uly_status check_attn(const char* fn, int64_t N, int hq, int hk, int D, int dt,
   CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
   CHECK(std::isfinite(scale) && scale > 0.f, ULY_ERR_INVALID_ARG, "%s: softmax_scale=%g must be finite and > 0", fn, (double)scale);
   CHECK(causal == 0 || causal == 1, ULY_ERR_INVALID_ARG, "%s: causal=%d must be 0 or 1", fn, causal);
-  CHECK(causal == 1, ULY_ERR_UNSUPPORTED, "%s: only causal attention is implemented", fn);
   CHECK(cu == nullptr || ndocs >= 1, ULY_ERR_INVALID_ARG, "%s: ndocs=%d must be >= 1 with cu_seqlens", fn, ndocs);
   CHECK(cu == nullptr || (reinterpret_cast<uintptr_t>(cu) & 3u) == 0, ULY_ERR_INVALID_ARG,
         "%s: cu_seqlens must be 4-byte aligned", fn);
@@ -109,6 +108,7 @@ uly_status check_attn(const char* fn, int64_t N, int hq, int hk, int D, int dt,
   d->cu = cu;
   d->ndocs = cu ? ndocs : 1;
   d->scale = scale;
+  d->causal = causal;
   return ULY_OK;
 }
 

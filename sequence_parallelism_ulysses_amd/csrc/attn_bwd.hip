@@ -1,4 +1,5 @@
-// Causal GQA / packed-document attention backward for one head group.
+// Causal (or document-only masked) GQA / packed-document attention backward
+// for one head group.
 //
 // Gradients of L = sum(dO * O) for O = softmax(scale * Q K^T + mask) V, with
 // the probabilities recomputed from the forward's log-sum-exp (training runs
@@ -185,9 +186,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   const int kw0 = kv0 + 32 * w;
   const bool active = kw0 < p.N;
   const int key = kw0 + l32;
-  const int my_de = doc_of(p.cu, p.ndocs, p.N, min(key, p.N - 1)).end;
-  const int w_de_first = doc_of(p.cu, p.ndocs, p.N, min(kw0, p.N - 1)).end;
-  const int w_de_last = doc_of(p.cu, p.ndocs, p.N, min(kw0 + 31, p.N - 1)).end;
+  const KeyBounds kbd(p, key, kw0);
+  const int my_lo = kbd.my_lo, my_de = kbd.my_de;
+  const int w_de_first = kbd.w_de_first, w_de_last = kbd.w_de_last;
 
   // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
   frag_t kf[C::KS], vf[C::KS];
@@ -203,11 +204,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dkt[db] = dvt[db] = f32x16_t{};
 
-  // Queries that can see any of the 128 keys: [kv0, end of the last key's
-  // document). The (q head, query tile) iterations over them, head-major, are
-  // split evenly between p.splits workgroups; this one takes [it0, it1).
+  // Queries that can see any of the 128 keys: [first_query(kv0), end of the
+  // last key's document). The (q head, query tile) iterations over them,
+  // head-major, are split evenly between p.splits workgroups; this one takes
+  // [it0, it1).
   const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + 32 * kWaves - 1, p.N - 1)).end;
-  const int qt0 = kv0 / BT;
+  const int qt0 = first_query(p, kv0) / BT;
   const int n_qt = (q_end - 1) / BT - qt0 + 1;
   const int n_it = n_qt * p.G;
   const int it0 = int(int64_t(n_it) * split / p.splits);
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
     const char* dr = st + C::X_BYTES;
     const float* fl = reinterpret_cast<const float*>(st + 2 * C::X_BYTES);
 
-    if (active && qs + BT - 1 >= kw0 && qs < w_de_last) {
+    if (active && qs + BT - 1 >= kbd.w_lo_first && qs < w_de_last) {
       f32x16_t s[2], dp[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = f32x16_t{};
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
           dp[qb] = mfma(b, vf[ks], dp[qb]);
         }
       }
-      const bool need_mask = (qs < kw0 + 31) || (qs + BT > w_de_first);
+      const bool need_mask = (qs < kbd.w_lo_last) || (qs + BT > w_de_first);
       float pv[32], dsv[32];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
             float e = fast_exp2(fmaf(s[qb][r], p.scale_log2, -lv[j]));
             if (need_mask) {
               const int q = qs + qi + j;
-              if (q < key || q >= my_de) e = 0.f;
+              if (q < my_lo || q >= my_de) e = 0.f;
             }
             pv[qb * 16 + r] = e;
             dsv[qb * 16 + r] = e * (dp[qb][r] - dv4[j]);
@@ -426,9 +428,8 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
   const bool active = qbase < p.N;
   const int wq_last = min(qbase + 31, p.N - 1);
   const int my_q = qbase + l32;
-  const int my_ds = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1)).start;
-  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
-  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+  const QueryBounds qbd(p, my_q, qbase, wq_last, active);
+  const int my_ds = qbd.my_ds, my_hi = qbd.my_hi;
   const bool q_ok = my_q < p.N;
   const float my_lse2 = q_ok ? p.lse[int64_t(head) * p.N + my_q] * kLog2e : 0.f;
   const float my_dlt = q_ok ? p.delta[int64_t(head) * p.N + my_q] : 0.f;
@@ -447,7 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
   for (int db = 0; db < C::DB; ++db) dqt[db] = f32x16_t{};
 
   const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
-  const int t0 = kv_begin / BT, t1 = (wg_q1 - 1) / BT;
+  const int kv_end = p.causal ? wg_q1 : doc_of(p.cu, p.ndocs, p.N, wg_q1 - 1).end;
+  const int t0 = kv_begin / BT, t1 = (kv_end - 1) / BT;
 
   KvTile<Tr, D> tile;
   tile.load(p, kvh, t0 * BT, tid);
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
     const char* kr = st;
     const char* vr = st + C::X_BYTES;
 
-    if (active && kv0 <= wq_last && kv0 + BT > w_ds_first) {
+    if (active && kv0 <= qbd.w_hi_last && kv0 + BT > qbd.w_ds_first) {
       f32x16_t s[2], dp[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16_t{};
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
           dp[kb] = mfma(b, df[ks], dp[kb]);
         }
       }
-      const bool need_mask = (kv0 + BT - 1 > qbase) || (kv0 < w_ds_last);
+      const bool need_mask = (kv0 + BT - 1 > qbd.w_hi_first) || (kv0 < qbd.w_ds_last);
       float dsv[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
           float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
           if (need_mask) {
             const int key = kv0 + kb * 32 + acc_row(r, half);
-            if (key > my_q || key < my_ds) e = 0.f;
+            if (key > my_hi || key < my_ds) e = 0.f;
           }
           dsv[kb * 16 + r] = e * (dp[kb][r] - my_dlt);
         }
@@ -567,9 +569,8 @@ void dq_bf16_kernel(BwdParams p) {
   const int wq_last = min(qbase + 31, p.N - 1);
   const int my_q = qbase + l32;
   const bool q_ok = my_q < p.N;
-  const int my_ds = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1)).start;
-  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
-  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+  const QueryBounds qbd(p, my_q, qbase, wq_last, active);
+  const int my_ds = qbd.my_ds, my_hi = qbd.my_hi;
   const float my_lse2 = q_ok ? p.lse2[int64_t(head) * p.N + my_q] : 0.f;
   const float my_dlt = q_ok ? p.delta[int64_t(head) * p.N + my_q] : 0.f;
 
@@ -587,7 +588,8 @@ void dq_bf16_kernel(BwdParams p) {
   for (int db = 0; db < C::DB; ++db) dqt[db] = f32x16_t{};
 
   const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
-  const int t0 = kv_begin / BT, t1 = (wg_q1 - 1) / BT;
+  const int kv_end = p.causal ? wg_q1 : doc_of(p.cu, p.ndocs, p.N, wg_q1 - 1).end;
+  const int t0 = kv_begin / BT, t1 = (kv_end - 1) / BT;
   const uint32_t kv_row = uint32_t(p.hk) * D * 2;
 
   auto issue = [&](int t) {
@@ -608,8 +610,8 @@ void dq_bf16_kernel(BwdParams p) {
     const lds_char* kr = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
     const lds_char* vr = kr + C::TB;
 
-    if (active && kv0 <= wq_last && kv0 + BT > w_ds_first) {
-      const bool need_mask = (kv0 + BT - 1 > qbase) || (kv0 < w_ds_last);
+    if (active && kv0 <= qbd.w_hi_last && kv0 + BT > qbd.w_ds_first) {
+      const bool need_mask = (kv0 + BT - 1 > qbd.w_hi_first) || (kv0 < qbd.w_ds_last);
       f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
@@ -626,7 +628,7 @@ void dq_bf16_kernel(BwdParams p) {
           float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
           if (need_mask) {
             const int k = kv0 + kb * 32 + acc_row(r, half);
-            if (k > my_q || k < my_ds) e = 0.f;
+            if (k > my_hi || k < my_ds) e = 0.f;
           }
           dsv[kb * 16 + r] = e * (dp[kb][r] - my_dlt);
         }
@@ -685,6 +687,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   p.Gw = std::gcd(p.G, kWaves);
   p.scale = d.scale;
   p.scale_log2 = d.scale * kLog2e;
+  p.causal = d.causal;
 
   const int64_t rows = d.N * d.hq;
   const int64_t rows_per_block = kThreads / (D * Tr::kElem / 16);

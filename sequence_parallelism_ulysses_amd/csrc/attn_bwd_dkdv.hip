@@ -64,13 +64,13 @@ void dkdv_bf16_kernel(BwdParams p) {
   const int kv0 = (int(blockIdx.x) / p.splits) * C::kKeys;  // first tiles carry the most causal work
   const int kw0 = kv0 + 32 * kb;
   const int key = kw0 + l32;
-  const int my_de = doc_of(p.cu, p.ndocs, p.N, min(key, p.N - 1)).end;
-  const int w_de_first = doc_of(p.cu, p.ndocs, p.N, min(kw0, p.N - 1)).end;
-  const int w_de_last = doc_of(p.cu, p.ndocs, p.N, min(kw0 + 31, p.N - 1)).end;
+  const KeyBounds kbd(p, key, kw0);
+  const int my_lo = kbd.my_lo, my_de = kbd.my_de;
+  const int w_de_first = kbd.w_de_first, w_de_last = kbd.w_de_last;
   const uint32_t q_row = uint32_t(p.hq) * D * 2;
 
-  // Queries that can see any of the 128 keys: [kv0, end of the last key's
-  // document). The (query tile, q head) iterations over them, tiles from the
+  // Queries that can see any of the 128 keys: [first_query(kv0), end of
+  // the last key's document). The (query tile, q head) iterations over them, tiles from the
   // last one down and heads innermost, are dealt round-robin to the p.splits
   // workgroups of the key block; this one runs its share as local
   // iterations [it0, it1). All workgroups thus walk the tiles in the same
@@ -78,7 +78,7 @@ void dkdv_bf16_kernel(BwdParams p) {
   // the same Q / dO tiles and share them in L2 instead of each fetching its
   // own from memory.
   const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + C::kKeys - 1, p.N - 1)).end;
-  const int qt0 = kv0 / C::QT;
+  const int qt0 = first_query(p, kv0) / C::QT;
   const int n_qt = (q_end - 1) / C::QT - qt0 + 1;
   const int n_it = n_qt * p.G;
   const int it0 = 0;
@@ -87,13 +87,13 @@ void dkdv_bf16_kernel(BwdParams p) {
   auto tile_q0 = [&](int it) { return (qt0 + n_qt - 1 - (split + it * p.splits) / p.G) * C::QT; };
   auto tile_head = [&](int it) { return kvh * p.G + (split + it * p.splits) % p.G; };
   auto stage = [&](int it) { return ring + ((it - it0) % C::NSTAGE) * C::STAGE; };
-  // does a key block (first key kb0, its documents ending by de_last) receive
-  // gradient from tile it?
-  auto sees_block = [&](int it, int kb0, int de_last) {
+  // does a key block (first key kb0, seen from query lo_first on, its
+  // documents ending by de_last) receive gradient from tile it?
+  auto sees_block = [&](int it, int kb0, int lo_first, int de_last) {
     const int qs = tile_q0(it);
-    return kb0 < p.N && qs + C::QT - 1 >= kb0 && qs < de_last;
+    return kb0 < p.N && qs + C::QT - 1 >= lo_first && qs < de_last;
   };
-  auto sees = [&](int it) { return sees_block(it, kw0, w_de_last); };
+  auto sees = [&](int it) { return sees_block(it, kw0, kbd.w_lo_first, w_de_last); };
   // P (slots 0, 1) and dS (slots 2, 3) fragments of tile it for key block b
   auto pds_at = [&](int it, int b, int slot) {
     return pds + (((it & 1) * 4 + b) * 4 + slot) * 1024 + lane * 16;
@@ -122,7 +122,7 @@ void dkdv_bf16_kernel(BwdParams p) {
         const lds_char* dt = qt + C::TQ;
         typedef __attribute__((address_space(3))) const float lds_float;
         lds_float* fl = (lds_float*)(qt + 2 * C::TQ);
-        const bool need_mask = (qs < kw0 + 31) || (qs + C::QT > w_de_first);
+        const bool need_mask = (qs < kbd.w_lo_last) || (qs + C::QT > w_de_first);
         // All operand reads of the tile go out before the first MFMA, so the
         // 2 KS products run back to back instead of each waiting on its read.
         bf16x8_t qa[C::KS], da[C::KS];
@@ -157,7 +157,7 @@ void dkdv_bf16_kernel(BwdParams p) {
               float e = fast_exp2(fmaf(s[r], p.scale_log2, -l4[r4][j]));
               if constexpr (decltype(masked)::value) {
                 const int q = qs + qi + j;
-                if (q < key || q >= my_de) e = 0.f;
+                if (q < my_lo || q >= my_de) e = 0.f;
               }
               pv[r] = e;
               dsv[r] = e * (dp[r] - d4[r4][j]);
@@ -169,7 +169,8 @@ void dkdv_bf16_kernel(BwdParams p) {
             *(lds_frag*)pds_at(it, kb, 2 + st2) = make_frag<TrBF16>(&dsv[st2 * 8]);
           }
         };
-        // the element-wise mask only on diagonal tiles and tiles crossing a document end
+        // the element-wise mask only on tiles before some key's first query (the
+        // diagonal tiles when causal) and tiles crossing a document end
         if (need_mask) probs(std::true_type{}); else probs(std::false_type{});
       } else if (it < it1) {
         // a consumer covers two key blocks and may still read this one's fragments
@@ -185,11 +186,12 @@ void dkdv_bf16_kernel(BwdParams p) {
   const int cw = w - 4;
   const bool dk_role = cw & 1;
   const int cb = 2 * (cw >> 1);
-  int cb_k0[2], cb_de[2];
+  int cb_k0[2], cb_lo[2], cb_de[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     cb_k0[b] = kv0 + 32 * (cb + b);
-    cb_de[b] = doc_of(p.cu, p.ndocs, p.N, min(cb_k0[b] + 31, p.N - 1)).end;
+    cb_lo[b] = uniform(first_query(p, cb_k0[b]));
+    cb_de[b] = uniform(doc_of(p.cu, p.ndocs, p.N, min(cb_k0[b] + 31, p.N - 1)).end);
   }
   f32x16_t acc[2][C::DB];
 #pragma unroll
@@ -224,7 +226,7 @@ void dkdv_bf16_kernel(BwdParams p) {
     // the stage of tile it-2 is free: its consumer pass ended last iteration
     if (it + 2 < it1) issue(it + 2);
     const int jt = it - 1;  // the tile the producers finished last iteration
-    if (jt >= it0 && (sees_block(jt, cb_k0[0], cb_de[0]) || sees_block(jt, cb_k0[1], cb_de[1]))) {
+    if (jt >= it0 && (sees_block(jt, cb_k0[0], cb_lo[0], cb_de[0]) || sees_block(jt, cb_k0[1], cb_lo[1], cb_de[1]))) {
       const lds_char* src = stage(jt) + src_off;
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2) {

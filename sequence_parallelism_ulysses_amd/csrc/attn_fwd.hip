@@ -1,4 +1,5 @@
-// Causal GQA / packed-document attention forward for one head group.
+// Causal (or document-only masked) GQA / packed-document attention forward
+// for one head group.
 //
 // Exact softmax attention computed in key tiles with an online (running-max)
 // softmax, so the N x N score matrix is never stored ("Ulysses Sequence
@@ -23,9 +24,11 @@
 // reductions plus one v_permlane32_swap between the two half-waves. The
 // probabilities are then already laid out as the B operand of O^T += V^T P^T.
 //
-// Masking (key j, query i): j <= i and j >= doc_start(i). Only the diagonal
-// tile and tiles crossing a document start are masked element-wise; tiles
-// that no row of a wave can see are skipped by that wave.
+// Masking (key j, query i): doc_start(i) <= j <= hi(i), with hi(i) = i for
+// causal attention and the last token of i's document otherwise. Only tiles
+// past some row's hi (the diagonal tile when causal) and tiles crossing a
+// document start are masked element-wise; tiles that no row of a wave can see
+// are skipped by that wave.
 #include <cmath>
 #include <numeric>
 
@@ -48,6 +51,7 @@ struct FwdParams {
   int ndocs;
   int N, hq, hk, G, Gw;
   int n_qtiles;
+  int causal;
   float scale_log2;
 };
 
@@ -126,14 +130,22 @@ void attn_fwd_kernel(FwdParams p) {
   const int wq_last = min(qbase + RW - 1, p.N - 1);
 
   // Query rows of this lane, their document starts, and the wave's bounds.
-  int my_q[QB], my_ds[QB];
+  // Row i sees keys [doc start, hi(i)]: hi(i) = i when causal, else the
+  // last token of its document.
+  int my_q[QB], my_ds[QB], my_hi[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     my_q[qb] = qbase + qb * 32 + l32;
-    my_ds[qb] = doc_of(p.cu, p.ndocs, p.N, min(my_q[qb], p.N - 1)).start;
+    const DocSpan dsp = doc_of(p.cu, p.ndocs, p.N, min(my_q[qb], p.N - 1));
+    my_ds[qb] = dsp.start;
+    my_hi[qb] = p.causal ? my_q[qb] : dsp.end - 1;
   }
-  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
-  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+  const DocSpan w_doc_first = doc_of(p.cu, p.ndocs, p.N, min(qbase, p.N - 1));
+  const DocSpan w_doc_last = doc_of(p.cu, p.ndocs, p.N, wq_last);
+  const int w_ds_first = active ? w_doc_first.start : 0;
+  const int w_ds_last = w_doc_last.start;
+  const int w_hi_first = p.causal ? qbase : w_doc_first.end - 1;
+  const int w_hi_last = p.causal ? wq_last : w_doc_last.end - 1;
 
   // Q fragments (B operand of S^T = K Q^T), zero past N.
   frag_t qf[QB][C::KS];
@@ -157,7 +169,8 @@ void attn_fwd_kernel(FwdParams p) {
   }
 
   const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
-  const int t0 = kv_begin / BN, t1 = (wg_q1 - 1) / BN;
+  const int kv_end = p.causal ? wg_q1 : doc_of(p.cu, p.ndocs, p.N, wg_q1 - 1).end;
+  const int t0 = kv_begin / BN, t1 = (kv_end - 1) / BN;
 
   Tile<Tr, D> tile;
   tile.load(p, kvh, t0 * BN, tid);
@@ -170,9 +183,10 @@ void attn_fwd_kernel(FwdParams p) {
     const char* lk = smem + ((t - t0) & 1) * (C::K_BYTES + C::V_BYTES);
     const char* lv = lk + C::K_BYTES;
 
-    if (active && kv0 <= wq_last && kv0 + BN > w_ds_first) {
-      // element-wise mask only on the diagonal tile and tiles crossing a document start
-      const bool need_mask = __builtin_expect(kv0 + BN - 1 > qbase || kv0 < w_ds_last, 0);
+    if (active && kv0 <= w_hi_last && kv0 + BN > w_ds_first) {
+      // element-wise mask only on tiles past some row's last visible key (the
+      // diagonal tile when causal) and tiles crossing a document start
+      const bool need_mask = __builtin_expect(kv0 + BN - 1 > w_hi_first || kv0 < w_ds_last, 0);
       // S^T tile: keys (2 blocks of 32) x this wave's query columns.
       f32x16_t s[2][QB];
 #pragma unroll
@@ -198,7 +212,7 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = kv0 + kb * 32 + acc_row(r, half);
-              if (key > my_q[qb] || key < my_ds[qb]) s[kb][qb][r] = -INFINITY;
+              if (key > my_hi[qb] || key < my_ds[qb]) s[kb][qb][r] = -INFINITY;
             }
         }
         float mt = -INFINITY;
@@ -325,9 +339,17 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const bool active = qbase < p.N;
   const int wq_last = min(qbase + 31, p.N - 1);
   const int my_q = qbase + l32;
-  const int my_ds = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1)).start;
-  const int w_ds_first = active ? doc_of(p.cu, p.ndocs, p.N, qbase).start : 0;
-  const int w_ds_last = doc_of(p.cu, p.ndocs, p.N, wq_last).start;
+  // Row i sees keys [doc start, hi(i)]: hi(i) = i when causal, else the
+  // last token of its document.
+  const DocSpan my_doc = doc_of(p.cu, p.ndocs, p.N, min(my_q, p.N - 1));
+  const int my_ds = my_doc.start;
+  const int my_hi = p.causal ? my_q : my_doc.end - 1;
+  const DocSpan w_doc_first = doc_of(p.cu, p.ndocs, p.N, min(qbase, p.N - 1));
+  const DocSpan w_doc_last = doc_of(p.cu, p.ndocs, p.N, wq_last);
+  const int w_ds_first = active ? w_doc_first.start : 0;
+  const int w_ds_last = w_doc_last.start;
+  const int w_hi_first = p.causal ? qbase : w_doc_first.end - 1;
+  const int w_hi_last = p.causal ? wq_last : w_doc_last.end - 1;
 
   // Q fragments (B operand of S^T = K Q^T), zero past N.
   bf16x8_t qf[C::KS];
@@ -349,7 +371,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   vo.init(lane);
 
   const int kv_begin = doc_of(p.cu, p.ndocs, p.N, wg_q0).start;
-  const int t0 = kv_begin / BN, t1 = (wg_q1 - 1) / BN;
+  const int kv_end = p.causal ? wg_q1 : doc_of(p.cu, p.ndocs, p.N, wg_q1 - 1).end;
+  const int t0 = kv_begin / BN, t1 = (kv_end - 1) / BN;
   const uint32_t kv_row = uint32_t(p.hk) * D * 2;
 
   // Group A (waves 0-3) runs tile t's products in the first phase of
@@ -377,7 +400,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   };
   auto sees = [&](int t) {
     const int kv0 = t * BN;
-    return active && kv0 <= wq_last && kv0 + BN > w_ds_first;
+    return active && kv0 <= w_hi_last && kv0 + BN > w_ds_first;
   };
   auto compute_s = [&](int t, f32x16_t (&s)[2]) {
     const lds_char* lk = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
@@ -403,15 +426,16 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   auto softmax_pv = [&](int t, f32x16_t (&s)[2]) {
     const int kv0 = t * BN;
     const lds_char* lv = smem + ((t - t0) % C::NSTAGE) * C::STAGE + C::TB;
-    // element-wise mask only on the diagonal tile and tiles crossing a document start
-    const bool need_mask = kv0 + BN - 1 > qbase || kv0 < w_ds_last;
+    // element-wise mask only on tiles past some row's last visible key (the
+    // diagonal tile when causal) and tiles crossing a document start
+    const bool need_mask = kv0 + BN - 1 > w_hi_first || kv0 < w_ds_last;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + acc_row(r, half);
-          if (key > my_q || key < my_ds) s[kb][r] = -INFINITY;
+          if (key > my_hi || key < my_ds) s[kb][r] = -INFINITY;
         }
     }
     float mt = -INFINITY;
@@ -521,6 +545,7 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, flo
   const int rows = 32 * (C::kWaves / p.Gw);
   p.n_qtiles = static_cast<int>((d.N + rows - 1) / rows);
   p.scale_log2 = d.scale * kLog2e;
+  p.causal = d.causal;
   dim3 grid(p.n_qtiles, d.hk * (p.G / p.Gw));
   attn_fwd_bf16_kernel<D><<<grid, C::kThreads, 0, stream>>>(p);
   return hipGetLastError();
@@ -546,6 +571,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const int rows = C::RW * (C::kWaves / p.Gw);
   p.n_qtiles = static_cast<int>((d.N + rows - 1) / rows);
   p.scale_log2 = d.scale * kLog2e;
+  p.causal = d.causal;
   dim3 grid(p.n_qtiles, d.hk * (p.G / p.Gw));
   attn_fwd_kernel<Tr, D><<<grid, C::kThreads, 0, stream>>>(p);
   return hipGetLastError();

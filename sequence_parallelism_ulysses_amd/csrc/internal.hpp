@@ -37,6 +37,7 @@ struct AttnDesc {
   const int32_t* cu;     // device, or nullptr
   int ndocs;             // number of documents (1 when cu is nullptr)
   float scale;
+  int causal;            // 1: key j visible to query i iff j <= i (and same document); 0: same document
 };
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

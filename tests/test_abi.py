@@ -145,7 +145,6 @@ def _fwd(**kw):
     (dict(scale=0.0), uly.ULY_ERR_INVALID_ARG, "softmax_scale"),
     (dict(scale=float("nan")), uly.ULY_ERR_INVALID_ARG, "softmax_scale"),
     (dict(scale=float("inf")), uly.ULY_ERR_INVALID_ARG, "softmax_scale"),
-    (dict(causal=0), uly.ULY_ERR_UNSUPPORTED, "causal"),
     (dict(causal=2), uly.ULY_ERR_INVALID_ARG, "causal=2"),
     (dict(cu=FAKE, nd=0), uly.ULY_ERR_INVALID_ARG, "ndocs=0"),
     (dict(cu=FAKE + 2, nd=3), uly.ULY_ERR_INVALID_ARG, "4-byte"),
@@ -173,7 +172,6 @@ def _bwd(**kw):
     (dict(do=FAKE + 2), uly.ULY_ERR_INVALID_ARG, "dout"),
     (dict(wsb=16), uly.ULY_ERR_INVALID_ARG, "workspace_bytes"),
     (dict(ws=None), uly.ULY_ERR_INVALID_ARG, "workspace"),
-    (dict(causal=0), uly.ULY_ERR_UNSUPPORTED, "causal"),
     (dict(D=256), uly.ULY_ERR_INVALID_ARG, "D=256"),
     (dict(N=-5), uly.ULY_ERR_INVALID_ARG, "N=-5"),
     (dict(gdt=5), uly.ULY_ERR_INVALID_ARG, "grad_dt"),

@@ -477,6 +477,86 @@ def test_backward_q_zero_closed_form():
         assert np.allclose(res["dv"][j, 0], want, atol=1e-13)
 
 
+# ------------------------------------------- attention with document-only masks
+def test_noncausal_backward_finite_differences():
+    """Document-only mask (every token of a document sees the whole document):
+    central differences of L = sum(dO * O), with O from the pure-Python loops,
+    against the oracle's analytic gradients (catches a causal bound left in the
+    backward, or a key-side bound taken from the query's document)."""
+    r = _rng(31)
+    N, hq, hk, D = 7, 2, 1, 3
+    cu = cu_from_lengths([4, 3])
+    q, k, v, do = (r.normal(size=s) for s in [(N, hq, D), (N, hk, D), (N, hk, D), (N, hq, D)])
+    res = attn_ref(q, k, v, 0.7, cu, do=do, causal=False, workers=1)
+    h = 1e-6
+
+    def loss(args):
+        O, _ = brute_attn(args["q"], args["k"], args["v"], 0.7, cu, causal=False)
+        return float((O * do).sum())
+    for name, x, grad in (("q", q, res["dq"]), ("k", k, res["dk"]), ("v", v, res["dv"])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args)
+            args[name] = xm
+            lm = loss(args)
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(fd - grad).max() / max(np.abs(grad).max(), 1e-30)
+        assert err < 1e-6, (name, err)
+
+
+def test_noncausal_q_zero_closed_form():
+    """Q = 0 with a document-only mask: every row of a document of length L
+    averages all its values, LSE = log L, and dV_j = sum_h sum_{i in doc}
+    dO_{h,i} / L."""
+    r = _rng(32)
+    lens = [5, 1, 0, 9]
+    N = sum(lens)
+    cu = cu_from_lengths(lens)
+    q = np.zeros((N, 2, 4))
+    k, v, do = r.normal(size=(N, 1, 4)), r.normal(size=(N, 1, 4)), r.normal(size=(N, 2, 4))
+    res = attn_ref(q, k, v, 0.6, cu, do=do, causal=False, workers=1)
+    for a, b in zip(cu[:-1], cu[1:]):
+        if a == b:
+            continue
+        L = b - a
+        mean_v = v[a:b, 0].mean(axis=0)
+        for i in range(a, b):
+            for h in range(2):
+                assert np.allclose(res["o"][i, h], mean_v, atol=1e-13)
+                assert abs(res["lse"][h, i] - math.log(L)) < 1e-13
+        want_dv = do[a:b].sum(axis=(0, 1)) / L
+        for j in range(a, b):
+            assert np.allclose(res["dv"][j, 0], want_dv, atol=1e-13)
+
+
+def test_noncausal_matches_torch_autograd():
+    """torch fp64 autograd through an explicit document-masked softmax."""
+    r = _rng(33)
+    lens = [7, 0, 12, 4]
+    N, hq, hk, D = sum(lens), 4, 2, 5
+    cu = cu_from_lengths(lens)
+    q, k, v, do = (r.normal(size=s) for s in [(N, hq, D), (N, hk, D), (N, hk, D), (N, hq, D)])
+    res = attn_ref(q, k, v, 0.5, cu, do=do, causal=False, workers=1)
+    doc = torch.tensor(np.repeat(np.arange(len(lens)), lens))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = doc[None, :] == doc[:, None]
+    outs = []
+    for h in range(hq):
+        sc = 0.5 * tq[:, h] @ tk[:, h // (hq // hk)].T
+        outs.append(torch.softmax(sc.masked_fill(~mask, float("-inf")), dim=1) @ tv[:, h // (hq // hk)])
+    o = torch.stack(outs, dim=1)
+    (o * torch.tensor(do)).sum().backward()
+    assert np.allclose(res["o"], o.detach().numpy(), atol=1e-13)
+    assert np.allclose(res["dq"], tq.grad.numpy(), atol=1e-12)
+    assert np.allclose(res["dk"], tk.grad.numpy(), atol=1e-12)
+    assert np.allclose(res["dv"], tv.grad.numpy(), atol=1e-12)
+
+
 def test_doc_tables_and_errors():
     doc, start = doc_tables(np.array([0, 3, 3, 5]), 5)
     assert list(doc) == [0, 0, 0, 2, 2]
