@@ -161,6 +161,42 @@ def fused_qkv_rates(uly, cfg, reps: int) -> dict:
     return res
 
 
+def chunked_fwd_rate(uly, cfg, qg, kg, vg, fwd_flop: int, full_ms: float, reps: int) -> dict:
+    """The forward computed ring-style on this GPU: the sequence in P chunks,
+    query chunk i against key chunks c < i (attn_fwd, causal = 0) and c = i
+    (causal), then attn_merge of the i+1 partial results. Same causal pairs
+    and FLOPs as the single attn_fwd call; reported beside it, not part of
+    the step."""
+    import torch
+    P, T, hq, D = cfg.P, cfg.T, cfg.hq, cfg.D
+    dev = qg.device
+    parts_o = [torch.empty((T, hq, D), dtype=qg.dtype, device=dev) for _ in range(P)]
+    parts_l = [torch.empty((hq, T), dtype=torch.float32, device=dev) for _ in range(P)]
+    o = torch.empty_like(qg)
+    lse = [torch.empty((hq, T), dtype=torch.float32, device=dev) for _ in range(P)]
+
+    def run():
+        for i in range(P):
+            qi = qg[i * T:(i + 1) * T]
+            for c in range(i + 1):
+                uly.attn_fwd(qi, kg[c * T:(c + 1) * T], vg[c * T:(c + 1) * T], parts_o[c], parts_l[c],
+                             cfg.scale, causal=int(c == i))
+            uly.attn_merge(parts_o[:i + 1], parts_l[:i + 1], o[i * T:(i + 1) * T], lse[i])
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tf = fwd_flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "vs_single_attn_fwd": round(full_ms / ms, 4), "chunks": P,
+            "calls": f"{P * (P + 1) // 2} attn_fwd + {P} attn_merge"}
+
+
 def _doc_starts(N, cu):
     cuv = np.array([0, N]) if cu is None else np.asarray(cu, dtype=np.int64)
     tok = np.arange(N)
@@ -316,6 +352,8 @@ def main() -> int:
         "calls": details,
     }
     line["fused_qkv"] = fused_qkv_rates(uly, cfg, args.steps)
+    if cu is None:
+        line["chunked_fwd"] = chunked_fwd_rate(uly, cfg, qg, kg, vg, fwd_flop, call_ms["attn_fwd"], max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cu, host, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -14,6 +14,7 @@
  *   ulysses_pack     sequence-sharded -> head-sharded layout for one head group
  *   attn_fwd         causal or document-masked (optionally packed-document) GQA
  *                    attention forward
+ *   attn_merge       combine attention results over disjoint key chunks (LSE merge)
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
  *   ulysses_pack_qkv / ulysses_unpack_qkv
@@ -168,6 +169,28 @@ uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float*
                     int64_t N, int hq, int hk, int D, uly_dtype dt,
                     const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                     hipStream_t stream);
+
+/*
+ * attn_merge -- combine attention results computed over disjoint sets of
+ * keys into the result over their union, as a ring of key/value chunks
+ * produces them ("Snowflake's Ulysses trick ...", third paragraph: the
+ * comparison with Ring Attention, which passes chunks around a ring). For
+ * every row i and local q head h, with parts c = 0 .. nparts-1:
+ *   lse[h][i] = log sum_c exp(lse_c[h][i])
+ *   o[i][h][:] = sum_c exp(lse_c[h][i] - lse[h][i]) * o_c[i][h][:]
+ * (fp32 arithmetic, max-shifted; o rounded to nearest even for bf16). A part
+ * whose lse is -inf (no visible key) contributes nothing; if every part's is,
+ * o = 0 and lse = -inf.
+ *
+ * o_parts   : host array of nparts device pointers to [N][hq][D] of dt, each
+ *             the normalised output over its key set (as attn_fwd writes it).
+ * lse_parts : host array of nparts device pointers to float32 [hq][N].
+ * o         : device [N][hq][D] of dt; lse : device float32 [hq][N]; neither
+ *             may alias a part.
+ * nparts in [1, ULY_MAX_P]; N in [1, 2^30]; hq in [1, 1024]; D in {64, 128}.
+ */
+uly_status attn_merge(const void* const* o_parts, const float* const* lse_parts, int nparts, int64_t N,
+                      int hq, int D, uly_dtype dt, void* o, float* lse, hipStream_t stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for

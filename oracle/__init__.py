@@ -16,6 +16,10 @@ What it computes (plain numpy, fp64 for all floating point):
                           the same redistributions for a fused QKV projection
                           output (query, key, value heads of a token side by
                           side), one packed tensor per section
+  merge_ref               attention over a union of disjoint key sets from
+                          the per-set results (log-sum-exp merge; the pages
+                          compare Ulysses with Ring Attention, which produces
+                          such per-chunk results)
   attn_ref                exact masked softmax attention per head and its
                           analytic gradients (the plain definition that tiled
                           attention reproduces; "Ulysses Sequence Parallelism
@@ -30,6 +34,7 @@ from .ref import (  # noqa: F401
     bf16_bits_to_f64,
     doc_tables,
     f32_bits_to_f64,
+    merge_ref,
     pack_qkv_ref,
     pack_ref,
     unpack_qkv_ref,

@@ -360,3 +360,30 @@ def attn_ref(q, k, v, scale: float, cu_seqlens=None, do=None, rows=None,
             res["dk"][r["lo"]:r["hi"], kvh, :] += r["dk"]
             res["dv"][r["lo"]:r["hi"], kvh, :] += r["dv"]
     return res
+
+
+# ---------------------------------------------------------------------------
+# merging attention results over disjoint key sets
+# ---------------------------------------------------------------------------
+def merge_ref(o_parts, lse_parts):
+    """Attention over a union of disjoint key sets from the results over each
+    set (the per-chunk results a ring of key/value chunks produces:
+    "Snowflake's Ulysses trick ...", third paragraph, on Ring Attention).
+    With c over the parts, per row i and head h:
+
+        lse = log sum_c exp(lse_c),   o = sum_c exp(lse_c - lse) o_c.
+
+    o_parts: arrays [N, hq, D]; lse_parts: arrays [hq, N] (natural log; -inf
+    for a row with no visible key in that part). fp64. A row whose parts are
+    all -inf gets o = 0 and lse = -inf."""
+    lse_all = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])   # [C, hq, N]
+    o_all = np.stack([np.asarray(x, dtype=np.float64) for x in o_parts])       # [C, N, hq, D]
+    m = lse_all.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_all), np.exp(lse_all - m_safe[None]), 0.0)    # [C, hq, N]
+    s = w.sum(axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, s, 1.0)), -np.inf)
+    wn = np.where(finite[None], w / np.where(finite, s, 1.0)[None], 0.0)      # [C, hq, N]
+    o = np.einsum("chn,cnhd->nhd", wn, o_all)
+    return o, lse

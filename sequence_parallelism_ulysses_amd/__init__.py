@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     attn_bwd,
     attn_bwd_workspace_size,
     attn_fwd,
+    attn_merge,
     last_error,
     lib,
     lib_path,

@@ -31,6 +31,7 @@ SIGNATURES = {
     "ulysses_unpack_qkv": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32,
                                    ctypes.POINTER(_vp), _vp]),
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32, _f32, _i32, _vp]),
+    "attn_merge": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
                         _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -193,6 +194,21 @@ def attn_fwd(q, k, v, o, lse, softmax_scale: float, cu_seqlens=None, causal: int
     cu, nd = _cu(cu_seqlens, N)
     _raise(lib().attn_fwd(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
                           _stream(stream)))
+
+
+def attn_merge(o_parts: Sequence, lse_parts: Sequence, o, lse, stream=None) -> None:
+    """o, lse = the merge of per-key-chunk results (see include/ulysses.h)."""
+    import torch
+    n = len(o_parts)
+    if n != len(lse_parts) or n < 1:
+        raise ValueError("need as many lse parts as output parts, at least one")
+    N, hq, D = o.shape
+    dt = o.dtype
+    op = (ctypes.c_void_p * n)(*[_dev(t, (N, hq, D), dt, f"o_parts[{c}]").value for c, t in enumerate(o_parts)])
+    lp = (ctypes.c_void_p * n)(*[_dev(t, (hq, N), torch.float32, f"lse_parts[{c}]").value
+                                 for c, t in enumerate(lse_parts)])
+    _raise(lib().attn_merge(op, lp, n, N, hq, D, _dtype_code(o), _dev(o, (N, hq, D), dt, "o"),
+                            _dev(lse, (hq, N), torch.float32, "lse"), _stream(stream)))
 
 
 def attn_bwd_workspace_size(N: int, hq: int, hk: int, D: int, dtype) -> int:

@@ -208,6 +208,29 @@ uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   return from_hip(uly::launch_attn_fwd(q, k, v, o, lse, d, stream), "attn_fwd");
 }
 
+uly_status attn_merge(const void* const* o_parts, const float* const* lse_parts, int nparts, int64_t N, int hq,
+                      int D, uly_dtype dt, void* o, float* lse, hipStream_t stream) {
+  CHECK(nparts >= 1 && nparts <= ULY_MAX_P, ULY_ERR_INVALID_ARG, "attn_merge: nparts=%d must be in [1, %d]", nparts,
+        ULY_MAX_P);
+  CHECK(N >= 1 && N <= (int64_t(1) << 30), ULY_ERR_INVALID_ARG, "attn_merge: N=%lld must be in [1, 2^30]",
+        (long long)N);
+  CHECK(hq >= 1 && hq <= 1024, ULY_ERR_INVALID_ARG, "attn_merge: hq=%d must be in [1, 1024]", hq);
+  CHECK(D == 64 || D == 128, ULY_ERR_INVALID_ARG, "attn_merge: D=%d must be 64 or 128", D);
+  CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "attn_merge: unknown dtype %d", (int)dt);
+  CHECK(o_parts != nullptr && lse_parts != nullptr, ULY_ERR_INVALID_ARG, "attn_merge: o_parts or lse_parts is NULL");
+  CHECK(o != nullptr && aligned16(o), ULY_ERR_INVALID_ARG, "attn_merge: o is NULL or not 16-byte aligned");
+  CHECK(lse != nullptr && aligned16(lse), ULY_ERR_INVALID_ARG, "attn_merge: lse is NULL or not 16-byte aligned");
+  for (int c = 0; c < nparts; ++c) {
+    CHECK(o_parts[c] != nullptr && aligned16(o_parts[c]), ULY_ERR_INVALID_ARG,
+          "attn_merge: o_parts[%d] is NULL or not 16-byte aligned", c);
+    CHECK(lse_parts[c] != nullptr && aligned16(lse_parts[c]), ULY_ERR_INVALID_ARG,
+          "attn_merge: lse_parts[%d] is NULL or not 16-byte aligned", c);
+    CHECK(o_parts[c] != o && lse_parts[c] != lse, ULY_ERR_INVALID_ARG,
+          "attn_merge: part %d aliases an output", c);
+  }
+  return from_hip(uly::launch_attn_merge(o_parts, lse_parts, nparts, N, hq, D, dt, o, lse, stream), "attn_merge");
+}
+
 uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype dt, size_t* bytes) {
   uly::AttnDesc d;
   uly_status s = check_attn("attn_bwd_workspace_size", N, hq, hk, D, dt, nullptr, 1, 1.0f, 1, &d);

@@ -43,6 +43,10 @@ struct AttnDesc {
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const AttnDesc& d, hipStream_t stream);
 
+// o = sum_c exp(lse_c - lse) o_c, lse = log sum_c exp(lse_c), per (row, head).
+hipError_t launch_attn_merge(const void* const* o_parts, const float* const* lse_parts, int nparts, int64_t N,
+                             int hq, int D, uly_dtype dt, void* o, float* lse, hipStream_t stream);
+
 size_t bwd_workspace_bytes(const AttnDesc& d);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,

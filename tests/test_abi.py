@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "uly_check_cu_seqlens", "uly_last_error",
+        "attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
         "ulysses_pack", "ulysses_pack_qkv", "ulysses_unpack", "ulysses_unpack_qkv"])
 
 
@@ -125,6 +125,26 @@ def test_pack_qkv_rejects(kw, status, needle):
 ])
 def test_unpack_qkv_rejects(kw, needle):
     assert _unpack_qkv(**kw) == uly.ULY_ERR_INVALID_ARG
+    assert needle in uly.last_error()
+
+
+def _merge(**kw):
+    a = dict(op=_ptrs(3), lp=_ptrs(3, base=FAKE + (1 << 20)), n=3, N=1024, hq=4, D=128, dt=uly.ULY_BF16,
+             o=FAKE + (2 << 20), lse=FAKE + (3 << 20), stream=None)
+    a.update(kw)
+    return uly.lib().attn_merge(a["op"], a["lp"], a["n"], a["N"], a["hq"], a["D"], a["dt"], a["o"], a["lse"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(n=0), "nparts=0"), (dict(n=65), "nparts=65"), (dict(N=0), "N=0"), (dict(hq=0), "hq=0"),
+    (dict(D=96), "D=96"), (dict(dt=9), "dtype"), (dict(op=None), "NULL"), (dict(o=None), "o is NULL"),
+    (dict(lse=FAKE + 4), "lse is NULL"), (dict(op=(ctypes.c_void_p * 3)(FAKE, None, FAKE)), "o_parts[1]"),
+    (dict(lp=(ctypes.c_void_p * 3)(FAKE, FAKE, FAKE + 8)), "lse_parts[2]"),
+    (dict(o=FAKE + 4096), "aliases"),
+])
+def test_merge_rejects(kw, needle):
+    assert _merge(**kw) == uly.ULY_ERR_INVALID_ARG
     assert needle in uly.last_error()
 
 

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attn_ref, bf16_bits_to_f64, doc_tables, f32_bits_to_f64, pack_qkv_ref, pack_ref,
+from oracle import (attn_ref, bf16_bits_to_f64, doc_tables, f32_bits_to_f64, merge_ref, pack_qkv_ref, pack_ref,
                     unpack_qkv_ref, unpack_ref)
 from synthetic import cu_from_lengths
 
@@ -555,6 +555,55 @@ def test_noncausal_matches_torch_autograd():
     assert np.allclose(res["dq"], tq.grad.numpy(), atol=1e-12)
     assert np.allclose(res["dk"], tk.grad.numpy(), atol=1e-12)
     assert np.allclose(res["dv"], tv.grad.numpy(), atol=1e-12)
+
+
+# ------------------------------------------------------------ LSE merge of key chunks
+def test_merge_of_key_chunks_equals_full_attention():
+    """Causal attention over N = 4 chunks of T tokens, computed chunk pair by
+    chunk pair (query chunk i against key chunk c: no mask for c < i, causal
+    within the chunk for c = i) and merged, equals attention over the whole
+    sequence (the identity ring-style attention rests on)."""
+    r = _rng(41)
+    P, T, hq, hk, D = 4, 9, 4, 2, 5
+    N = P * T
+    q, k, v = r.normal(size=(N, hq, D)), r.normal(size=(N, hk, D)), r.normal(size=(N, hk, D))
+    full = attn_ref(q, k, v, 0.6, workers=1)
+    for i in range(P):
+        qi = slice(i * T, (i + 1) * T)
+        parts = []
+        for c in range(i + 1):
+            kc = slice(c * T, (c + 1) * T)
+            parts.append(attn_ref(q[qi], k[kc], v[kc], 0.6, causal=(c == i), workers=1))
+        o, lse = merge_ref([p["o"] for p in parts], [p["lse"] for p in parts])
+        assert np.allclose(o, full["o"][qi], atol=1e-12)
+        assert np.allclose(lse, full["lse"][:, qi], atol=1e-12)
+
+
+def test_merge_brute_force_and_edge_cases():
+    """Explicit loops with math.exp/log; one part is the identity; parts
+    commute; a part with lse = -inf adds nothing; all parts -inf -> o = 0,
+    lse = -inf."""
+    r = _rng(42)
+    N, hq, D, C = 5, 2, 3, 3
+    o_parts = [r.normal(size=(N, hq, D)) for _ in range(C)]
+    lse_parts = [r.normal(size=(hq, N)) * 3 for _ in range(C)]
+    o, lse = merge_ref(o_parts, lse_parts)
+    for h in range(hq):
+        for i in range(N):
+            z = sum(math.exp(lse_parts[c][h, i]) for c in range(C))
+            assert abs(lse[h, i] - math.log(z)) < 1e-12
+            for d in range(D):
+                want = sum(math.exp(lse_parts[c][h, i]) / z * o_parts[c][i, h, d] for c in range(C))
+                assert abs(o[i, h, d] - want) < 1e-12
+    o1, l1 = merge_ref(o_parts[:1], lse_parts[:1])
+    assert np.allclose(o1, o_parts[0], atol=1e-15) and np.allclose(l1, lse_parts[0], atol=1e-15)
+    o2, l2 = merge_ref(o_parts[::-1], lse_parts[::-1])
+    assert np.allclose(o2, o, atol=1e-13) and np.allclose(l2, lse, atol=1e-13)
+    dead = np.full((hq, N), -np.inf)
+    o3, l3 = merge_ref(o_parts + [r.normal(size=(N, hq, D))], lse_parts + [dead])
+    assert np.allclose(o3, o, atol=1e-13) and np.allclose(l3, lse, atol=1e-13)
+    o4, l4 = merge_ref(o_parts[:2], [dead, dead])
+    assert np.all(o4 == 0) and np.all(l4 == -np.inf)
 
 
 def test_doc_tables_and_errors():
