@@ -13,7 +13,7 @@ Metric: algorithmic causal-attention fwd+bwd TFLOP/s of the step
 roofline of the dominant call and the oracle timed on the host as a baseline.
 Prints one JSON line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3] [--no-side-legs]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
                                              scaling rocprofv3 byte counters)
 """
@@ -212,6 +212,8 @@ def main() -> int:
     ap.add_argument("--config", default="c3", help="workload key: c3 (default), c2, c4, c5")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-legs", action="store_true",
+                    help="skip the fused-QKV and chunked-forward measurements (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.copy_calibration:
@@ -351,8 +353,9 @@ def main() -> int:
         "roofline": roofline,
         "calls": details,
     }
-    line["fused_qkv"] = fused_qkv_rates(uly, cfg, args.steps)
-    if cu is None:
+    if not args.no_side_legs:
+        line["fused_qkv"] = fused_qkv_rates(uly, cfg, args.steps)
+    if cu is None and not args.no_side_legs:
         line["chunked_fwd"] = chunked_fwd_rate(uly, cfg, qg, kg, vg, fwd_flop, call_ms["attn_fwd"], max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cu, host, args.cpu_seconds)

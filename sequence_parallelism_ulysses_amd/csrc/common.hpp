@@ -81,6 +81,52 @@ __device__ __forceinline__ DocSpan doc_of(const int32_t* __restrict__ cu, int nd
   return {cu[lo], cu[hi]};
 }
 
+// Launch order by causal work with packed documents. Query tile q covers
+// rows [q*R, (q+1)*R); under the causal mask its work grows with its
+// position k = q - floor(cu_d / R) counted from the first tile of the
+// document d that holds its first row. Tiles whose first row lies in
+// document d have the keys a_d .. e_d, one tile each, with
+//   a_d = ceil(cu_d / R) - floor(cu_d / R),  e_d = ceil(cu_{d+1} / R) - 1 - floor(cu_d / R),
+// and these ranges cover all ceil(N / R) tiles once. Returns the tile of rank
+// b (0-based) in the order (key descending, document descending): the key by
+// a binary search on C(k) = number of tiles with key >= k, a sum over the
+// documents with one lane per document, then the document by its rank among
+// those holding that key. Every lane returns the same tile. Requires
+// 1 <= ndocs <= 64 and valid cu_seqlens; without documents the order is
+// simply q = n_tiles - 1 - b.
+__device__ __forceinline__ int tile_by_work_rank(const int32_t* __restrict__ cu, int ndocs, int R, int n_tiles,
+                                                 int b) {
+  const int lane = threadIdx.x & 63;
+  int a = 1, e = 0, base = 0;  // lanes without a document hold an empty range
+  if (lane < ndocs) {
+    const int c0 = cu[lane], c1 = cu[lane + 1];
+    base = c0 / R;
+    a = (c0 + R - 1) / R - base;
+    e = (c1 + R - 1) / R - 1 - base;
+  }
+  auto count_ge = [&](int k) {
+    const int lo = a > k ? a : k;
+    int c = e >= lo ? e - lo + 1 : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m);
+    return c;
+  };
+  // largest key k with C(k) > b: C(0) = n_tiles > b and C(n_tiles) = 0
+  int lo = 0, hi = n_tiles;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count_ge(mid) > b) lo = mid; else hi = mid;
+  }
+  const int j = b - count_ge(lo + 1);  // rank among the documents holding key lo
+  const bool has = lane < ndocs && a <= lo && lo <= e;
+  const uint64_t mask = __ballot(has);
+  const int above = __popcll((mask >> lane) >> 1);  // documents after this lane's holding key lo
+  const uint64_t pick = __ballot(has && above == j);
+  const int d = pick ? __ffsll(static_cast<unsigned long long>(pick)) - 1 : 0;
+  const int q = __shfl(base, d) + lo;
+  return q < 0 ? 0 : (q >= n_tiles ? n_tiles - 1 : q);
+}
+
 // Element traits: bf16 uses v_mfma_f32_32x32x16_bf16 (8 k-values per lane),
 // fp32 uses v_mfma_f32_32x32x2f32 (1 k-value per lane).
 struct TrBF16 {
