@@ -100,16 +100,28 @@ def test_bwd_small_full(N, P, Hq, Hkv, D, dtype, lens):
     check_grads(cfg, got, oracle_attention(run))
 
 
-def test_bwd_many_documents_full():
-    """Dozens of short documents (and an empty one): the bf16 kernels then run
-    their blocks in an order sorted by work, which must still cover every block
-    exactly once."""
-    rng = np.random.default_rng(123)
+def _doc_lengths(total_tokens, max_len, seed, ndocs=None):
+    rng = np.random.default_rng(seed)
+    if ndocs is not None:   # exactly ndocs documents (one empty), random cuts
+        cuts = np.sort(rng.choice(np.arange(1, total_tokens), size=ndocs - 2, replace=False))
+        return [0] + np.diff(np.concatenate([[0], cuts, [total_tokens]])).tolist()
     lens, total = [0], 0
-    while total < 8192:
-        lens.append(int(rng.integers(1, 600)))
+    while total < total_tokens:
+        lens.append(int(rng.integers(1, max_len)))
         total += lens[-1]
-    lens[-1] -= total - 8192
+    lens[-1] -= total - total_tokens
+    return lens
+
+
+@pytest.mark.parametrize("max_len,ndocs", [(600, None), (128, None), (None, 64), (None, 65)])
+def test_bwd_many_documents_full(max_len, ndocs):
+    """Many short documents (and an empty one). With up to 64 documents the
+    forward and dQ kernels launch their query tiles in work order (a rank ->
+    tile map computed in the kernel), which must cover every tile exactly
+    once; with more they use the sequence order. Dozens of documents, about
+    120, and exactly 64 and 65 (the switch between the two)."""
+    lens = _doc_lengths(8192, max_len, seed=123 + (ndocs or 0), ndocs=ndocs)
+    assert ndocs is None or len(lens) == ndocs
     cfg = syn.custom(8192, 8, 32, 8, 128, "bf16", seed=99)
     run = Run(cfg, cu=syn.cu_from_lengths(lens))
     got = run_fwd_bwd(run)
