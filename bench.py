@@ -161,40 +161,63 @@ def fused_qkv_rates(uly, cfg, reps: int) -> dict:
     return res
 
 
-def chunked_fwd_rate(uly, cfg, qg, kg, vg, fwd_flop: int, full_ms: float, reps: int) -> dict:
-    """The forward computed ring-style on this GPU: the sequence in P chunks,
-    query chunk i against key chunks c < i (attn_fwd, causal = 0) and c = i
-    (causal), then attn_merge of the i+1 partial results. Same causal pairs
-    and FLOPs as the single attn_fwd call; reported beside it, not part of
-    the step."""
+def chunked_rates(uly, cfg, qg, kg, vg, dog, fwd_flop: int, bwd_flop: int, call_ms: dict, reps: int) -> dict:
+    """Attention computed ring-style on this GPU: the sequence in P chunks;
+    forward = query chunk i against key chunks c < i (attn_fwd, causal = 0)
+    and c = i (causal), then attn_merge of the i+1 partial results; backward =
+    one attn_bwd_accumulate per chunk pair into float32 gradients (zeroed
+    first). Same causal pairs and FLOPs as the single calls; reported beside
+    them, not part of the step."""
     import torch
-    P, T, hq, D = cfg.P, cfg.T, cfg.hq, cfg.D
+    P, T, hq, hk, D = cfg.P, cfg.T, cfg.hq, cfg.hk, cfg.D
     dev = qg.device
     parts_o = [torch.empty((T, hq, D), dtype=qg.dtype, device=dev) for _ in range(P)]
     parts_l = [torch.empty((hq, T), dtype=torch.float32, device=dev) for _ in range(P)]
     o = torch.empty_like(qg)
     lse = [torch.empty((hq, T), dtype=torch.float32, device=dev) for _ in range(P)]
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.zeros(qg.shape, **f32), torch.zeros(kg.shape, **f32), torch.zeros(vg.shape, **f32)
+    ws = torch.empty(uly.attn_bwd_workspace_size(T, hq, hk, D, qg.dtype), dtype=torch.uint8, device=dev)
 
-    def run():
+    def fwd():
         for i in range(P):
             qi = qg[i * T:(i + 1) * T]
             for c in range(i + 1):
                 uly.attn_fwd(qi, kg[c * T:(c + 1) * T], vg[c * T:(c + 1) * T], parts_o[c], parts_l[c],
                              cfg.scale, causal=int(c == i))
             uly.attn_merge(parts_o[:i + 1], parts_l[:i + 1], o[i * T:(i + 1) * T], lse[i])
-    run()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        run()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    tf = fwd_flop / (ms * 1e-3) / 1e12
-    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "vs_single_attn_fwd": round(full_ms / ms, 4), "chunks": P,
-            "calls": f"{P * (P + 1) // 2} attn_fwd + {P} attn_merge"}
+
+    def bwd():
+        for t in (dq, dk, dv):
+            t.zero_()
+        for i in range(P):
+            r = slice(i * T, (i + 1) * T)
+            for c in range(i + 1):
+                kc = slice(c * T, (c + 1) * T)
+                uly.attn_bwd_accumulate(qg[r], kg[kc], vg[kc], o[r], dog[r], lse[i], dq[r], dk[kc], dv[kc],
+                                        cfg.scale, ws, causal=int(c == i))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {"chunks": P, "calls": f"fwd: {P * (P + 1) // 2} attn_fwd + {P} attn_merge; "
+                                 f"bwd: {P * (P + 1) // 2} attn_bwd_accumulate (fp32 gradients)"}
+    for name, fn, flop, single in (("fwd", fwd, fwd_flop, "attn_fwd"), ("bwd", bwd, bwd_flop, "attn_bwd")):
+        ms = timed(fn)
+        tf = flop / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     f"vs_single_{single}": round(call_ms[single] / ms, 4)}
+    del parts_o, parts_l, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def _doc_starts(N, cu):
@@ -356,7 +379,8 @@ def main() -> int:
     if not args.no_side_legs:
         line["fused_qkv"] = fused_qkv_rates(uly, cfg, args.steps)
     if cu is None and not args.no_side_legs:
-        line["chunked_fwd"] = chunked_fwd_rate(uly, cfg, qg, kg, vg, fwd_flop, call_ms["attn_fwd"], max(3, args.steps // 4))
+        line["chunked"] = chunked_rates(uly, cfg, qg, kg, vg, dog, fwd_flop, bwd_flop, call_ms,
+                                        max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, cu, host, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -16,6 +16,7 @@
  *                    attention forward
  *   attn_merge       combine attention results over disjoint key chunks (LSE merge)
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
+ *   attn_bwd_accumulate  the same, adding to the gradients (chunked attention)
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
  *   ulysses_pack_qkv / ulysses_unpack_qkv
  *                    the same for a fused QKV projection output, one launch
@@ -225,6 +226,24 @@ uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                     int64_t N, int hq, int hk, int D, uly_dtype dt, uly_dtype grad_dt,
                     const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_bwd_accumulate -- attn_bwd that adds its gradients to dq, dk and dv
+ * instead of overwriting them. This is what the backward of attention over
+ * key/value chunks needs (the chunks of Ring Attention, "Snowflake's Ulysses
+ * trick ...", third paragraph): with o and lse the merged results over all
+ * chunks (attn_merge), one call per (query chunk, key chunk) pair adds that
+ * pair's share to the query chunk's dq and the key chunk's dk and dv, and
+ * the sums equal the gradients of attention over the union.
+ * Same arguments and preconditions as attn_bwd, except that grad_dt must be
+ * ULY_F32 (accumulating in bf16 would round at every call; otherwise
+ * ULY_ERR_UNSUPPORTED) and dq, dk, dv must hold the values to add to.
+ */
+uly_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               int64_t N, int hq, int hk, int D, uly_dtype dt, uly_dtype grad_dt,
+                               const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * Never NULL; valid until the next call on the same thread. */

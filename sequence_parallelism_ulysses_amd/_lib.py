@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
                         _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd_accumulate": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
+                                   _vp, _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
     "uly_last_error": (ctypes.c_char_p, []),
     "uly_check_cu_seqlens": (_i32, [ctypes.POINTER(ctypes.c_int32), _i32, _i64]),
 }
@@ -222,6 +224,17 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace,
              causal: int = 1, stream=None) -> None:
     """Gradients dq, dk, dv of sum(dout * o) (see include/ulysses.h). The
     gradient type (grad_dt) is taken from dq: the input type, or float32."""
+    _bwd("attn_bwd", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream)
+
+
+def attn_bwd_accumulate(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, cu_seqlens=None,
+                        causal: int = 1, stream=None) -> None:
+    """attn_bwd adding to float32 dq, dk, dv (see include/ulysses.h)."""
+    _bwd("attn_bwd_accumulate", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal,
+         stream)
+
+
+def _bwd(fn, q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream):
     import torch
     N, hq, D = q.shape
     hk = k.shape[1]
@@ -235,8 +248,8 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace,
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     cu, nd = _cu(cu_seqlens, N)
-    _raise(lib().attn_bwd(*args, N, hq, hk, D, _dtype_code(q), _dtype_code(dq), cu, nd, float(softmax_scale), int(causal),
-                          ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream)))
+    _raise(getattr(lib(), fn)(*args, N, hq, hk, D, _dtype_code(q), _dtype_code(dq), cu, nd, float(softmax_scale),
+                              int(causal), ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream)))
 
 
 def uly_check_cu_seqlens(host_cu, N: int) -> None:

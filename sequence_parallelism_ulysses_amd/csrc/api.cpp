@@ -109,6 +109,7 @@ uly_status check_attn(const char* fn, int64_t N, int hq, int hk, int D, int dt,
   d->ndocs = cu ? ndocs : 1;
   d->scale = scale;
   d->causal = causal;
+  d->accumulate = 0;
   return ULY_OK;
 }
 
@@ -240,28 +241,55 @@ uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype d
   return ULY_OK;
 }
 
-uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
-                    uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale,
-                    int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+uly_status bwd_common(const char* fn, int accumulate, const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk,
+                      int D, uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs,
+                      float softmax_scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   uly::AttnDesc d;
-  uly_status s = check_attn("attn_bwd", N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
+  uly_status s = check_attn(fn, N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
   if (s != ULY_OK) return s;
-  CHECK(valid_dtype(grad_dt), ULY_ERR_INVALID_ARG, "attn_bwd: unknown grad_dt %d", (int)grad_dt);
+  CHECK(valid_dtype(grad_dt), ULY_ERR_INVALID_ARG, "%s: unknown grad_dt %d", fn, (int)grad_dt);
   CHECK(grad_dt == dt || grad_dt == ULY_F32, ULY_ERR_UNSUPPORTED,
-        "attn_bwd: grad_dt must equal dt or be ULY_F32", 0);
+        "%s: grad_dt must equal dt or be ULY_F32", fn);
+  CHECK(!accumulate || grad_dt == ULY_F32, ULY_ERR_UNSUPPORTED,
+        "%s: accumulating gradients requires grad_dt ULY_F32", fn);
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 9; ++i)
     CHECK(ptrs[i] != nullptr && aligned16(ptrs[i]), ULY_ERR_INVALID_ARG,
-          "attn_bwd: %s is NULL or not 16-byte aligned", names[i]);
+          "%s: %s is NULL or not 16-byte aligned", fn, names[i]);
   const size_t need = uly::bwd_workspace_bytes(d);
-  CHECK(workspace_bytes >= need, ULY_ERR_INVALID_ARG, "attn_bwd: workspace_bytes=%zu < required %zu",
+  CHECK(workspace_bytes >= need, ULY_ERR_INVALID_ARG, "%s: workspace_bytes=%zu < required %zu", fn,
         workspace_bytes, need);
   CHECK(need == 0 || (workspace != nullptr && aligned16(workspace)), ULY_ERR_INVALID_ARG,
-        "attn_bwd: workspace is NULL or not 16-byte aligned");
-  return from_hip(uly::launch_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, grad_dt, stream),
-                  "attn_bwd");
+        "%s: workspace is NULL or not 16-byte aligned", fn);
+  d.accumulate = accumulate;
+  return from_hip(uly::launch_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, d, grad_dt, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
+                    uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale,
+                    int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common("attn_bwd", 0, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, grad_dt, cu_seqlens, ndocs,
+                    softmax_scale, causal, workspace, workspace_bytes, stream);
+}
+
+uly_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
+                               uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs,
+                               float softmax_scale, int causal, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return bwd_common("attn_bwd_accumulate", 1, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, grad_dt,
+                    cu_seqlens, ndocs, softmax_scale, causal, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -326,8 +326,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
           kx[j] = dkt[db][4 * r4 + j] * p.scale;
           vx[j] = dvt[db][4 * r4 + j];
         }
-        store4<kF32Out>(p.dk + off + d * OE, kx);
-        store4<kF32Out>(p.dv + off + d * OE, vx);
+        store4<kF32Out>(p.dk + off + d * OE, kx, p.accumulate);
+        store4<kF32Out>(p.dv + off + d * OE, vx, p.accumulate);
       }
   }
 }
@@ -353,8 +353,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int 
 #pragma unroll
   for (int j = 0; j < 4; ++j) k[j] *= p.scale;
   constexpr int OE = kF32Out ? 4 : 2;
-  store4<kF32Out>(p.dk + 4 * i * OE, k);
-  store4<kF32Out>(p.dv + 4 * i * OE, v);
+  store4<kF32Out>(p.dk + 4 * i * OE, k, p.accumulate);
+  store4<kF32Out>(p.dv + 4 * i * OE, v, p.accumulate);
 }
 
 // ----------------------------------------------------------------------------
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = dqt[db][4 * r4 + j] * p.scale;
-        store4<kF32Out>(dst + d * OE, x);
+        store4<kF32Out>(dst + d * OE, x, p.accumulate);
       }
   }
 }
@@ -658,7 +658,7 @@ void dq_bf16_kernel(BwdParams p) {
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = dqt[db][4 * r4 + j] * p.scale;
-        store4<kF32Out>(dst + d * OE, x);
+        store4<kF32Out>(dst + d * OE, x, p.accumulate);
       }
   }
 }
@@ -692,6 +692,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   p.scale = d.scale;
   p.scale_log2 = d.scale * kLog2e;
   p.causal = d.causal;
+  p.accumulate = d.accumulate;
 
   const int64_t rows = d.N * d.hq;
   const int64_t rows_per_block = kThreads / (D * Tr::kElem / 16);

@@ -273,7 +273,7 @@ void dkdv_bf16_kernel(BwdParams p) {
           float x[4];
 #pragma unroll
           for (int j2 = 0; j2 < 4; ++j2) x[j2] = acc[b][db][4 * r4 + j2] * mul;
-          store4<kF32Out>(out + off + d * OE, x);
+          store4<kF32Out>(out + off + d * OE, x, p.accumulate);
         }
     }
   }

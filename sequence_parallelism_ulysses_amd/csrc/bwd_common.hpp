@@ -29,6 +29,7 @@ struct BwdParams {
   int n_tiles;
   int splits;  // workgroups sharing one dK/dV key tile
   int causal;  // 1: key j visible to query i iff j <= i (and same document); 0: same document
+  int accumulate;  // 1: add the gradients to dq, dk, dv (fp32 outputs only) instead of overwriting
   float scale, scale_log2;
 };
 
@@ -81,12 +82,19 @@ __device__ __forceinline__ int first_query(const BwdParams& p, int k0) {
 }
 
 // Store 4 consecutive gradient values as fp32 (16 bytes) or bf16 (8 bytes,
-// rounded to nearest even).
+// rounded to nearest even). With `add` (fp32 only) the values are added to
+// what the destination holds.
 template <bool kF32>
-__device__ __forceinline__ void store4(char* dst, const float (&x)[4]) {
+__device__ __forceinline__ void store4(char* dst, const float (&x)[4], bool add = false) {
   if constexpr (kF32) {
+    float y[4] = {x[0], x[1], x[2], x[3]};
+    if (add) {
+      const f32x4_t old = *reinterpret_cast<const f32x4_t*>(dst);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = old[j] + y[j];
+    }
     *reinterpret_cast<u32x4_t*>(dst) =
-        u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+        u32x4_t{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
   } else {
     *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
   }

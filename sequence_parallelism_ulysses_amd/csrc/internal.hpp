@@ -38,6 +38,7 @@ struct AttnDesc {
   int ndocs;             // number of documents (1 when cu is nullptr)
   float scale;
   int causal;            // 1: key j visible to query i iff j <= i (and same document); 0: same document
+  int accumulate;        // backward only: add to dq, dk, dv (fp32 gradients) instead of overwriting
 };
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

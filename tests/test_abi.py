@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
+        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_workspace_size", "attn_fwd", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
         "ulysses_pack", "ulysses_pack_qkv", "ulysses_unpack", "ulysses_unpack_qkv"])
 
 
@@ -177,12 +177,12 @@ def test_attn_fwd_rejects(kw, status, needle):
     assert needle in uly.last_error()
 
 
-def _bwd(**kw):
+def _bwd(fn="attn_bwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, N=1024, hq=4, hk=1,
              D=128, dt=uly.ULY_BF16, gdt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, ws=FAKE, wsb=1 << 30,
              stream=None)
     a.update(kw)
-    return uly.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["N"],
+    return getattr(uly.lib(), fn)(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["N"],
                               a["hq"], a["hk"], a["D"], a["dt"], a["gdt"], a["cu"], a["nd"], a["scale"], a["causal"], a["ws"],
                               a["wsb"], a["stream"])
 
@@ -200,6 +200,15 @@ def _bwd(**kw):
 def test_attn_bwd_rejects(kw, status, needle):
     assert _bwd(**kw) == status
     assert needle in uly.last_error()
+    acc_kw = dict(gdt=uly.ULY_F32)
+    acc_kw.update(kw)
+    assert _bwd("attn_bwd_accumulate", **acc_kw) == status
+    assert needle in uly.last_error()
+
+
+def test_attn_bwd_accumulate_needs_fp32_gradients():
+    assert _bwd("attn_bwd_accumulate", gdt=uly.ULY_BF16) == uly.ULY_ERR_UNSUPPORTED
+    assert "ULY_F32" in uly.last_error()
 
 
 def test_workspace_size():

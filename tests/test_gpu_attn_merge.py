@@ -1,6 +1,7 @@
 """GPU parity of attn_merge, and of causal attention computed chunk by chunk
 and merged (ring-style: query chunk i against key chunks c <= i) against the
-fp64 oracle's attention over the whole sequence.
+fp64 oracle's attention over the whole sequence; the same for the backward
+through attn_bwd_accumulate, and the accumulate semantics themselves.
 
 Tolerances: the merge alone is fp32 arithmetic rounded once, so bf16 outputs
 must be within half a bf16 ulp of the exact merge plus 1e-5 (fp32 outputs:
@@ -57,10 +58,11 @@ def test_merge_matches_oracle(N, hq, D, C, dtype):
     assert np.all(got_o[5, 0] == 0)
 
 
-def chunked_causal_fwd(q, k, v, scale, P):
+def chunked_causal_fwd(q, k, v, scale, P, chunk_lse=None):
     """Causal attention of [N][hq][D] tensors in P equal chunks: for query
     chunk i, attn_fwd against key chunk c < i (no mask) and c = i (causal),
-    then attn_merge of the i+1 partial results."""
+    then attn_merge of the i+1 partial results. chunk_lse, if a list, gets
+    each query chunk's merged [hq][T] LSE."""
     N, hq, D = q.shape
     T = N // P
     o = torch.empty_like(q)
@@ -79,7 +81,29 @@ def chunked_causal_fwd(q, k, v, scale, P):
         uly.attn_merge(o_parts, l_parts, oi, li)
         o[i * T:(i + 1) * T] = oi
         lse[:, i * T:(i + 1) * T] = li
+        if chunk_lse is not None:
+            chunk_lse.append(li)
     return o, lse
+
+
+def chunked_causal_bwd(q, k, v, o, do, chunk_lse, scale, P):
+    """The backward of chunked_causal_fwd: one attn_bwd_accumulate per
+    (query chunk i, key chunk c <= i) pair, with the merged O and LSE of
+    chunk i, into zeroed float32 dq, dk, dv."""
+    N, hq, D = q.shape
+    T = N // P
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.zeros(q.shape, **f32)
+    dk = torch.zeros(k.shape, **f32)
+    dv = torch.zeros(v.shape, **f32)
+    ws = torch.empty(uly.attn_bwd_workspace_size(T, hq, k.shape[1], D, q.dtype), dtype=torch.uint8, device=q.device)
+    for i in range(P):
+        r = slice(i * T, (i + 1) * T)
+        for c in range(i + 1):
+            kc = slice(c * T, (c + 1) * T)
+            uly.attn_bwd_accumulate(q[r], k[kc], v[kc], o[r], do[r], chunk_lse[i], dq[r], dk[kc], dv[kc], scale,
+                                    ws, causal=int(c == i))
+    return dq, dk, dv
 
 
 @pytest.mark.parametrize("N,P,Hq,Hkv,D,dtype", [(8192, 8, 32, 8, 128, "bf16"), (1000, 4, 8, 8, 64, "f32"),
@@ -99,3 +123,52 @@ def test_chunked_attention_equals_full(N, P, Hq, Hkv, D, dtype):
     else:
         assert_close(got_o, ref["o"], bf16_tol(ref["o"]), "O")
         assert_close(lse.cpu().numpy().astype(np.float64), ref["lse"], 1e-3, "LSE")
+
+
+@pytest.mark.parametrize("N,P,Hq,Hkv,D,dtype", [(4096, 4, 32, 8, 128, "bf16"), (1000, 4, 8, 8, 64, "f32"),
+                                                 (1200, 6, 12, 6, 128, "bf16")])
+def test_chunked_backward_equals_full(N, P, Hq, Hkv, D, dtype):
+    """Forward and backward over P chunks (merged forward, then one
+    accumulating backward call per chunk pair) against the oracle's
+    gradients over the whole sequence: fp32 gradients within 2e-2 (bf16
+    inputs) or 1e-4 (fp32)."""
+    cfg = syn.custom(N, P, Hq, Hkv, D, dtype, seed=N + 23)
+    run = Run(cfg)
+    q, k, v, do = run.packed("q"), run.packed("k"), run.packed("v"), run.packed("do")
+    lses = []
+    o, _ = chunked_causal_fwd(q, k, v, cfg.scale, P, chunk_lse=lses)
+    dq, dk, dv = chunked_causal_bwd(q, k, v, o, do, lses, cfg.scale, P)
+    torch.cuda.synchronize()
+    x = run.oracle_inputs()
+    ref = attn_ref(x["q"], x["k"], x["v"], cfg.scale, do=x["do"])
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(t.cpu().numpy().astype(np.float64), ref[name], tol, name)
+
+
+@pytest.mark.parametrize("N,hq,hk,dtype", [(1000, 4, 1, "bf16"), (333, 2, 2, "f32"), (131072, 4, 2, "bf16")])
+def test_bwd_accumulate_adds_to_the_outputs(N, hq, hk, dtype):
+    """attn_bwd_accumulate into buffers holding E gives E + (what attn_bwd
+    writes) bit for bit (both paths compute the same fp32 values; one fp32 add).
+    The 131072-token case runs the dK/dV kernel without split partials, the
+    others through the split reduce."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(N + hq)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    D = 128
+    q = torch.randn((N, hq, D), generator=g, device=DEV).to(tdt)
+    k, v = (torch.randn((N, hk, D), generator=g, device=DEV).to(tdt) for _ in range(2))
+    do = torch.randn((N, hq, D), generator=g, device=DEV).to(tdt)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, N), dtype=torch.float32, device=DEV)
+    scale = D ** -0.5
+    uly.attn_fwd(q, k, v, o, lse, scale)
+    ws = torch.empty(uly.attn_bwd_workspace_size(N, hq, hk, D, tdt), dtype=torch.uint8, device=DEV)
+    plain = [torch.empty(t.shape, dtype=torch.float32, device=DEV) for t in (q, k, v)]
+    uly.attn_bwd(q, k, v, o, do, lse, *plain, scale, ws)
+    prior = [torch.randn(t.shape, generator=g, device=DEV) for t in (q, k, v)]
+    acc = [t.clone() for t in prior]
+    uly.attn_bwd_accumulate(q, k, v, o, do, lse, *acc, scale, ws)
+    torch.cuda.synchronize()
+    for name, a, e, x in zip(("dq", "dk", "dv"), acc, prior, plain):
+        assert torch.equal(a, e + x), name
