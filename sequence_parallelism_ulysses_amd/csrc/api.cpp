@@ -82,8 +82,9 @@ uly_status check_permute_qkv(const char* fn, int P, int64_t T, int Hq, int Hkv, 
   out->head_offset[0] = group * hq * D * e;
   out->head_offset[1] = (int64_t(Hq) + group * hk) * D * e;
   out->head_offset[2] = (int64_t(Hq) + Hkv + group * hk) * D * e;
-  CHECK(T * (out->seg_bytes[0] / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
-        "%s: one shard's query head group (%lld bytes) exceeds 32 GiB", fn, (long long)(T * out->seg_bytes[0]));
+  for (int sg = 0; sg < 3; ++sg)
+    CHECK(T * (out->seg_bytes[sg] / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
+          "%s: one shard's head group (%lld bytes) exceeds 32 GiB", fn, (long long)(T * out->seg_bytes[sg]));
   return ULY_OK;
 }
 
@@ -218,6 +219,8 @@ uly_status attn_merge(const void* const* o_parts, const float* const* lse_parts,
   CHECK(hq >= 1 && hq <= 1024, ULY_ERR_INVALID_ARG, "attn_merge: hq=%d must be in [1, 1024]", hq);
   CHECK(D == 64 || D == 128, ULY_ERR_INVALID_ARG, "attn_merge: D=%d must be 64 or 128", D);
   CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "attn_merge: unknown dtype %d", (int)dt);
+  CHECK(N * hq * D / 8 < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
+        "attn_merge: N * hq * D = %lld elements exceeds 2^34", (long long)(N * hq * D));
   CHECK(o_parts != nullptr && lse_parts != nullptr, ULY_ERR_INVALID_ARG, "attn_merge: o_parts or lse_parts is NULL");
   CHECK(o != nullptr && aligned16(o), ULY_ERR_INVALID_ARG, "attn_merge: o is NULL or not 16-byte aligned");
   CHECK(lse != nullptr && aligned16(lse), ULY_ERR_INVALID_ARG, "attn_merge: lse is NULL or not 16-byte aligned");

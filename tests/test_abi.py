@@ -113,6 +113,7 @@ def _unpack_qkv(**kw):
     (dict(v=FAKE + 8), uly.ULY_ERR_INVALID_ARG, "v_out"),
     (dict(shards=(ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))), uly.ULY_ERR_INVALID_ARG, "shards[7]"),
     (dict(T=1 << 26, Hq=64, Hkv=8, P=1, shards=_ptrs(1)), uly.ULY_ERR_UNSUPPORTED, "32 GiB"),
+    (dict(T=1 << 26, Hq=8, Hkv=64, P=1, shards=_ptrs(1)), uly.ULY_ERR_UNSUPPORTED, "32 GiB"),
 ])
 def test_pack_qkv_rejects(kw, status, needle):
     assert _pack_qkv(**kw) == status
@@ -146,6 +147,11 @@ def _merge(**kw):
 def test_merge_rejects(kw, needle):
     assert _merge(**kw) == uly.ULY_ERR_INVALID_ARG
     assert needle in uly.last_error()
+
+
+def test_merge_rejects_grids_beyond_2_31_threads():
+    assert _merge(N=1 << 30, hq=1024) == uly.ULY_ERR_UNSUPPORTED
+    assert "2^34" in uly.last_error()
 
 
 def _fwd(**kw):
