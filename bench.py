@@ -71,10 +71,12 @@ def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
         pairs = int((rows - start[rows] + 1).sum())
         return dt, pairs
 
+    # probe, then size R so that the measured run takes about budget_s (the
+    # cost of a row is about proportional to the keys it sees)
     R = min(cfg.N, 64)
     dt, pairs = run(R)
-    while dt < budget_s / 4 and R < cfg.N:
-        R = min(cfg.N, int(R * max(2.0, min(8.0, budget_s / max(dt, 1e-3) / 2))))
+    while dt < budget_s / 2 and R < cfg.N:
+        R = min(cfg.N, int(R * max(1.5, min(8.0, budget_s / max(dt, 1e-3)))))
         dt, pairs = run(R)
     flops = 14 * cfg.D * cfg.hq * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
