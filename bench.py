@@ -3,10 +3,12 @@
 
 One step = the whole hot path over one batch of synthetic input, with every
 input already resident in HBM:
-  pack Q, K, V, dO (sequence-sharded -> head group)   4 x ulysses_pack
-  causal attention forward                             attn_fwd
-  causal attention backward                            attn_bwd
-  unpack O, dQ, dK, dV (head group -> sequence-sharded) 4 x ulysses_unpack
+  pack Q, K, V (sequence-sharded -> head group)      ulysses_pack_multi
+  pack dO                                            ulysses_pack
+  causal attention forward                           attn_fwd
+  causal attention backward                          attn_bwd
+  unpack O (head group -> sequence-sharded)          ulysses_unpack
+  unpack dQ, dK, dV                                  ulysses_unpack_multi
 
 Metric: algorithmic causal-attention fwd+bwd TFLOP/s of the step
 (14 * D * C * hq FLOP, C = number of causal (query, key) pairs), with the
@@ -281,17 +283,17 @@ def main() -> int:
     out_sh = {n: [torch.zeros((T, cfg.heads(n), D), dtype=tdt, device=dev) for _ in range(P)]
               for n in ("o", "dq", "dk", "dv")}
 
+    # Q, K and V are regrouped together after the projections, dQ, dK and dV
+    # together after the backward: one launch each (ulysses_pack_multi)
+    qkv_sh = [shards["q"], shards["k"], shards["v"]]
+    dqkv_sh = [out_sh["dq"], out_sh["dk"], out_sh["dv"]]
     calls = [
-        ("pack_q", lambda: uly.ulysses_pack(shards["q"], g, qg)),
-        ("pack_k", lambda: uly.ulysses_pack(shards["k"], g, kg)),
-        ("pack_v", lambda: uly.ulysses_pack(shards["v"], g, vg)),
+        ("pack_qkv", lambda: uly.ulysses_pack_multi(qkv_sh, g, [qg, kg, vg])),
         ("pack_do", lambda: uly.ulysses_pack(shards["do"], g, dog)),
         ("attn_fwd", lambda: uly.attn_fwd(qg, kg, vg, o, lse, cfg.scale, cu_dev)),
         ("attn_bwd", lambda: uly.attn_bwd(qg, kg, vg, o, dog, lse, dq, dk, dv, cfg.scale, ws, cu_dev)),
         ("unpack_o", lambda: uly.ulysses_unpack(o, g, out_sh["o"])),
-        ("unpack_dq", lambda: uly.ulysses_unpack(dq, g, out_sh["dq"])),
-        ("unpack_dk", lambda: uly.ulysses_unpack(dk, g, out_sh["dk"])),
-        ("unpack_dv", lambda: uly.ulysses_unpack(dv, g, out_sh["dv"])),
+        ("unpack_dqkv", lambda: uly.ulysses_unpack_multi([dq, dk, dv], g, dqkv_sh)),
     ]
 
     def step(events=None):
@@ -326,7 +328,7 @@ def main() -> int:
     value = step_flop / (ms_step * 1e-3) / 1e12
 
     def pack_bytes(name):
-        heads = hq if name.endswith(("_q", "_do", "_o", "_dq")) else hk
+        heads = {"pack_qkv": hq + 2 * hk, "unpack_dqkv": hq + 2 * hk, "pack_do": hq, "unpack_o": hq}[name]
         return 2 * N * heads * D * 2
     details = {}
     for name, ms in call_ms.items():

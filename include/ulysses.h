@@ -18,6 +18,8 @@
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   attn_bwd_accumulate  the same, adding to the gradients (chunked attention)
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
+ *   ulysses_pack_multi / ulysses_unpack_multi
+ *                    the same for up to three tensors in one launch
  *   ulysses_pack_qkv / ulysses_unpack_qkv
  *                    the same for a fused QKV projection output, one launch
  *
@@ -104,6 +106,34 @@ uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int 
  */
 uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt,
                           int group, void* const* shards, hipStream_t stream);
+
+/*
+ * ulysses_pack_multi -- ulysses_pack of up to three tensors in one launch,
+ * e.g. Q, K and V as their projections leave them, each sequence-sharded
+ * with its own head count. For tensor i and its hh_i = H[i]/P heads:
+ *
+ *   outs[i][j*T + t][h][:] = shards[i*P + j][t][group*hh_i + h][:]
+ *
+ * ntensors in [1, 3]. shards: host array of ntensors*P device pointers,
+ * tensor-major, each [T][H[i]][D]. H: host array of ntensors head counts.
+ * outs: host array of ntensors device pointers, outs[i] [P*T][hh_i][D]
+ * (written in full). P, T, D, dt and group are shared; each tensor must
+ * satisfy the ulysses_pack preconditions. Bit-exact.
+ */
+uly_status ulysses_pack_multi(int ntensors, const void* const* shards, const int* H, int P, int64_t T,
+                              int D, uly_dtype dt, int group, void* const* outs, hipStream_t stream);
+
+/*
+ * ulysses_unpack_multi -- ulysses_unpack of up to three tensors in one launch
+ * (e.g. dQ, dK and dV back to their sequence-sharded gradients):
+ *
+ *   shards[i*P + j][t][group*hh_i + h][:] = ins[i][j*T + t][h][:]
+ *
+ * Only the group's heads are written; every other head is left untouched.
+ * Arguments as ulysses_pack_multi with ins[i] the [P*T][hh_i][D] inputs.
+ */
+uly_status ulysses_unpack_multi(int ntensors, const void* const* ins, const int* H, int P, int64_t T,
+                                int D, uly_dtype dt, int group, void* const* shards, hipStream_t stream);
 
 /*
  * ulysses_pack_qkv -- ulysses_pack for the output of a fused QKV projection,

@@ -26,6 +26,10 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "ulysses_pack": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
+    "ulysses_pack_multi": (_i32, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, _i64, _i32, _i32, _i32,
+                                   ctypes.POINTER(_vp), _vp]),
+    "ulysses_unpack_multi": (_i32, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, _i64, _i32, _i32, _i32,
+                                     ctypes.POINTER(_vp), _vp]),
     "ulysses_pack_qkv": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                  _vp]),
     "ulysses_unpack_qkv": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32,
@@ -147,6 +151,40 @@ def ulysses_unpack(inp, group: int, shards: Sequence, stream=None) -> None:
         _dev(inp, (P * T, H // P, D), dt, "inp")
     _raise(lib().ulysses_unpack(ctypes.c_void_p(inp.data_ptr()), P, T, H, D, _dtype_code(shards[0]), group,
                                 ptrs, _stream(stream)))
+
+
+def _multi(tensors, packed, name):
+    n = len(tensors)
+    if n < 1 or n != len(packed):
+        raise ValueError("need one packed tensor per shard list, at least one")
+    P = len(tensors[0])
+    T, _, D = tensors[0][0].shape
+    dt = tensors[0][0].dtype
+    ptrs, heads = [], []
+    for i, sh in enumerate(tensors):
+        if len(sh) != P:
+            raise ValueError("every tensor needs the same number of shards")
+        H = sh[0].shape[1]
+        heads.append(H)
+        ptrs += [_dev(s, (T, H, D), dt, f"{name}[{i}][{j}]").value for j, s in enumerate(sh)]
+        if H % P == 0:
+            _dev(packed[i], (P * T, H // P, D), dt, f"packed[{i}]")
+    return (n, (ctypes.c_void_p * len(ptrs))(*ptrs), (ctypes.c_int * n)(*heads), P, T, D, _dtype_code(tensors[0][0]),
+            (ctypes.c_void_p * n)(*[t.data_ptr() for t in packed]))
+
+
+def ulysses_pack_multi(tensors: Sequence, group: int, outs: Sequence, stream=None) -> None:
+    """ulysses_pack of up to three tensors in one launch: tensors[i] is the
+    list of P shards of tensor i (see include/ulysses.h)."""
+    n, ptrs, heads, P, T, D, dt, packed = _multi(tensors, outs, "tensors")
+    _raise(lib().ulysses_pack_multi(n, ptrs, heads, P, T, D, dt, group, packed, _stream(stream)))
+
+
+def ulysses_unpack_multi(ins: Sequence, group: int, tensors: Sequence, stream=None) -> None:
+    """ulysses_unpack of up to three tensors in one launch; heads outside the
+    group are untouched."""
+    n, ptrs, heads, P, T, D, dt, packed = _multi(tensors, ins, "tensors")
+    _raise(lib().ulysses_unpack_multi(n, packed, heads, P, T, D, dt, group, ptrs, _stream(stream)))
 
 
 def _qkv_shards(shards, Hq: int, Hkv: int):

@@ -50,7 +50,7 @@ uly_status check_permute(const char* fn, int P, int64_t T, int H, int D, int dt,
   const int64_t hh = H / P;
   out->P = P;
   out->T = T;
-  out->row_bytes = H * D * e;
+  out->row_bytes[0] = H * D * e;
   out->nseg = 1;
   out->seg_bytes[0] = hh * D * e;
   out->head_offset[0] = group * hh * D * e;
@@ -75,7 +75,7 @@ uly_status check_permute_qkv(const char* fn, int P, int64_t T, int Hq, int Hkv, 
   const int64_t hq = Hq / P, hk = Hkv / P;
   out->P = P;
   out->T = T;
-  out->row_bytes = int64_t(Hq + 2 * Hkv) * D * e;
+  out->row_bytes[0] = out->row_bytes[1] = out->row_bytes[2] = int64_t(Hq + 2 * Hkv) * D * e;
   out->nseg = 3;
   out->seg_bytes[0] = hq * D * e;
   out->seg_bytes[1] = out->seg_bytes[2] = hk * D * e;
@@ -143,7 +143,8 @@ uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int 
     CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
           "ulysses_pack: shards[%d] is NULL or not 16-byte aligned", j);
   void* const outs[1] = {out};
-  return from_hip(uly::launch_pack(shards, outs, d, stream), "ulysses_pack");
+  const void* const* sh[1] = {shards};
+  return from_hip(uly::launch_pack(sh, outs, d, stream), "ulysses_pack");
 }
 
 uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt, int group,
@@ -157,7 +158,8 @@ uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dt
     CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
           "ulysses_unpack: shards[%d] is NULL or not 16-byte aligned", j);
   const void* const ins[1] = {in};
-  return from_hip(uly::launch_unpack(ins, shards, d, stream), "ulysses_unpack");
+  void* const* sh[1] = {shards};
+  return from_hip(uly::launch_unpack(ins, sh, d, stream), "ulysses_unpack");
 }
 
 uly_status ulysses_pack_qkv(const void* const* shards, int P, int64_t T, int Hq, int Hkv, int D,
@@ -175,7 +177,8 @@ uly_status ulysses_pack_qkv(const void* const* shards, int P, int64_t T, int Hq,
   for (int j = 0; j < P; ++j)
     CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
           "ulysses_pack_qkv: shards[%d] is NULL or not 16-byte aligned", j);
-  return from_hip(uly::launch_pack(shards, outs, d, stream), "ulysses_pack_qkv");
+  const void* const* sh[3] = {shards, shards, shards};
+  return from_hip(uly::launch_pack(sh, outs, d, stream), "ulysses_pack_qkv");
 }
 
 uly_status ulysses_unpack_qkv(const void* dq, const void* dk, const void* dv, int P, int64_t T, int Hq,
@@ -193,7 +196,74 @@ uly_status ulysses_unpack_qkv(const void* dq, const void* dk, const void* dv, in
   for (int j = 0; j < P; ++j)
     CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
           "ulysses_unpack_qkv: shards[%d] is NULL or not 16-byte aligned", j);
-  return from_hip(uly::launch_unpack(ins, shards, d, stream), "ulysses_unpack_qkv");
+  void* const* sh[3] = {shards, shards, shards};
+  return from_hip(uly::launch_unpack(ins, sh, d, stream), "ulysses_unpack_qkv");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Several tensors, each with its own shards and head count, in one launch.
+uly_status check_permute_multi(const char* fn, int ntensors, const int* H, int P, int64_t T, int D, int dt,
+                               int group, uly::PermuteDesc* out) {
+  CHECK(ntensors >= 1 && ntensors <= ULY_PERMUTE_MAX_SEGMENTS, ULY_ERR_INVALID_ARG,
+        "%s: ntensors=%d must be in [1, %d]", fn, ntensors, ULY_PERMUTE_MAX_SEGMENTS);
+  CHECK(H != nullptr, ULY_ERR_INVALID_ARG, "%s: H is NULL", fn);
+  for (int i = 0; i < ntensors; ++i) {
+    uly::PermuteDesc one;
+    char name[64];
+    snprintf(name, sizeof name, "%s (tensor %d)", fn, i);
+    uly_status s = check_permute(name, P, T, H[i], D, dt, group, &one);
+    if (s != ULY_OK) return s;
+    out->row_bytes[i] = one.row_bytes[0];
+    out->seg_bytes[i] = one.seg_bytes[0];
+    out->head_offset[i] = one.head_offset[0];
+  }
+  out->P = P;
+  out->T = T;
+  out->nseg = ntensors;
+  return ULY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uly_status ulysses_pack_multi(int ntensors, const void* const* shards, const int* H, int P, int64_t T, int D,
+                              uly_dtype dt, int group, void* const* outs, hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_permute_multi("ulysses_pack_multi", ntensors, H, P, T, D, dt, group, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr && outs != nullptr, ULY_ERR_INVALID_ARG, "ulysses_pack_multi: shards or outs is NULL");
+  const void* const* sh[ULY_PERMUTE_MAX_SEGMENTS] = {};
+  for (int i = 0; i < ntensors; ++i) {
+    CHECK(outs[i] != nullptr && aligned16(outs[i]), ULY_ERR_INVALID_ARG,
+          "ulysses_pack_multi: outs[%d] is NULL or not 16-byte aligned", i);
+    for (int j = 0; j < P; ++j)
+      CHECK(shards[i * P + j] != nullptr && aligned16(shards[i * P + j]), ULY_ERR_INVALID_ARG,
+            "ulysses_pack_multi: shards[%d] is NULL or not 16-byte aligned", i * P + j);
+    sh[i] = shards + i * P;
+  }
+  return from_hip(uly::launch_pack(sh, outs, d, stream), "ulysses_pack_multi");
+}
+
+uly_status ulysses_unpack_multi(int ntensors, const void* const* ins, const int* H, int P, int64_t T, int D,
+                                uly_dtype dt, int group, void* const* shards, hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_permute_multi("ulysses_unpack_multi", ntensors, H, P, T, D, dt, group, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr && ins != nullptr, ULY_ERR_INVALID_ARG, "ulysses_unpack_multi: shards or ins is NULL");
+  void* const* sh[ULY_PERMUTE_MAX_SEGMENTS] = {};
+  for (int i = 0; i < ntensors; ++i) {
+    CHECK(ins[i] != nullptr && aligned16(ins[i]), ULY_ERR_INVALID_ARG,
+          "ulysses_unpack_multi: ins[%d] is NULL or not 16-byte aligned", i);
+    for (int j = 0; j < P; ++j)
+      CHECK(shards[i * P + j] != nullptr && aligned16(shards[i * P + j]), ULY_ERR_INVALID_ARG,
+            "ulysses_unpack_multi: shards[%d] is NULL or not 16-byte aligned", i * P + j);
+    sh[i] = shards + i * P;
+  }
+  return from_hip(uly::launch_unpack(ins, sh, d, stream), "ulysses_unpack_multi");
 }
 
 uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t N,

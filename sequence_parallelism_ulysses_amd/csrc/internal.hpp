@@ -12,22 +12,22 @@ namespace uly {
 
 #define ULY_PERMUTE_MAX_SEGMENTS 3
 
-// Byte-level description of one pack/unpack call: nseg segments of every
-// shard token (one for a single tensor; Q, K, V for a fused QKV tensor), each
-// moved to or from its own packed tensor.
+// Byte-level description of one pack/unpack call: nseg segments (one for a
+// single tensor; Q, K, V of a fused QKV tensor or of three tensors), each
+// moved between its own shards and its own packed tensor.
 struct PermuteDesc {
   int P;
   int64_t T;             // tokens per shard
-  int64_t row_bytes;     // bytes of one shard token (all its heads)
   int nseg;              // 1 .. ULY_PERMUTE_MAX_SEGMENTS
+  int64_t row_bytes[ULY_PERMUTE_MAX_SEGMENTS];    // bytes of one shard token of segment s (all its heads)
   int64_t seg_bytes[ULY_PERMUTE_MAX_SEGMENTS];    // hh * D * elem of segment s
   int64_t head_offset[ULY_PERMUTE_MAX_SEGMENTS];  // byte offset of segment s in a shard token
 };
 
-// out / in: nseg packed tensors, one per segment.
-hipError_t launch_pack(const void* const* shards, void* const* out, const PermuteDesc& d,
+// shards[s]: the P shard pointers of segment s; out / in: nseg packed tensors.
+hipError_t launch_pack(const void* const* const* shards, void* const* out, const PermuteDesc& d,
                        hipStream_t stream);
-hipError_t launch_unpack(const void* const* in, void* const* shards, const PermuteDesc& d,
+hipError_t launch_unpack(const void* const* in, void* const* const* shards, const PermuteDesc& d,
                          hipStream_t stream);
 
 struct AttnDesc {

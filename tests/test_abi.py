@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_bwd", "attn_bwd_accumulate", "attn_bwd_workspace_size", "attn_fwd", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
-        "ulysses_pack", "ulysses_pack_qkv", "ulysses_unpack", "ulysses_unpack_qkv"])
+        "ulysses_pack", "ulysses_pack_multi", "ulysses_pack_qkv", "ulysses_unpack", "ulysses_unpack_multi",
+        "ulysses_unpack_qkv"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -152,6 +153,32 @@ def test_merge_rejects(kw, needle):
 def test_merge_rejects_grids_beyond_2_31_threads():
     assert _merge(N=1 << 30, hq=1024) == uly.ULY_ERR_UNSUPPORTED
     assert "2^34" in uly.last_error()
+
+
+def _multi(fn="ulysses_pack_multi", **kw):
+    a = dict(n=3, shards=_ptrs(24), H=(ctypes.c_int * 3)(32, 8, 8), P=8, T=4096, D=128, dt=uly.ULY_BF16, group=0,
+             packed=_ptrs(3, base=FAKE + (1 << 24)), stream=None)
+    a.update(kw)
+    return getattr(uly.lib(), fn)(a["n"], a["shards"] if fn == "ulysses_pack_multi" else a["packed"], a["H"], a["P"],
+                                  a["T"], a["D"], a["dt"], a["group"],
+                                  a["packed"] if fn == "ulysses_pack_multi" else a["shards"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["ulysses_pack_multi", "ulysses_unpack_multi"])
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n=0), uly.ULY_ERR_INVALID_ARG, "ntensors=0"),
+    (dict(n=4), uly.ULY_ERR_INVALID_ARG, "ntensors=4"),
+    (dict(H=None), uly.ULY_ERR_INVALID_ARG, "H is NULL"),
+    (dict(H=(ctypes.c_int * 3)(32, 12, 8)), uly.ULY_ERR_INVALID_ARG, "tensor 1"),
+    (dict(D=96), uly.ULY_ERR_INVALID_ARG, "D=96"),
+    (dict(group=8), uly.ULY_ERR_INVALID_ARG, "group=8"),
+    (dict(shards=(ctypes.c_void_p * 24)(*([FAKE] * 20 + [None] + [FAKE] * 3))), uly.ULY_ERR_INVALID_ARG, "shards[20]"),
+    (dict(packed=(ctypes.c_void_p * 3)(FAKE, FAKE + 8, FAKE)), uly.ULY_ERR_INVALID_ARG, "[1] is NULL or not"),
+    (dict(T=1 << 26, H=(ctypes.c_int * 3)(64, 8, 8), P=1, shards=_ptrs(3)), uly.ULY_ERR_UNSUPPORTED, "32 GiB"),
+])
+def test_multi_rejects(fn, kw, status, needle):
+    assert _multi(fn, **kw) == status
+    assert needle in uly.last_error()
 
 
 def _fwd(**kw):

@@ -179,3 +179,39 @@ def test_pack_qkv_equals_separate_packs():
     rows = torch.from_numpy(np.concatenate([j * T + ts for j in range(P)])).to(DEV)
     for f, w in zip(fused, want):
         assert np.array_equal(dev_to_bits(f[rows]), w)
+
+
+MULTI_CASES = [
+    # (P, T, head counts, D, dtype)
+    (8, 4096, (32, 8, 8), 128, "bf16"),   # Q, K, V shards of the Llama-3.1-8B-shaped 32k workload
+    (4, 256, (8, 8, 8), 64, "f32"),       # the tiny fp32 shapes
+    (3, 37, (6, 3, 9), 64, "bf16"),       # ragged T, three different head counts
+    (2, 3000, (16, 4), 128, "bf16"),      # two tensors, partial last blocks
+    (1, 5, (4,), 128, "bf16"),            # one tensor, one rank
+    (64, 2, (64, 64, 128), 64, "bf16"),   # the largest rank count
+]
+
+
+@pytest.mark.parametrize("P,T,heads,D,dtype", MULTI_CASES)
+def test_pack_unpack_multi_bit_exact(P, T, heads, D, dtype):
+    """Several tensors in one launch against the oracle tensor by tensor, bit
+    for bit with random bit patterns; the inverse into canary-filled shards."""
+    host = [_host_shards(P, T, H, D, dtype, seed=31 * i + T) for i, H in enumerate(heads)]
+    dev = [[bits_to_dev(s) for s in h] for h in host]
+    tdt = dev[0][0].dtype
+    for g in sorted({0, P - 1, P // 2}):
+        outs = [torch.empty((P * T, H // P, D), dtype=tdt, device=DEV) for H in heads]
+        uly.ulysses_pack_multi(dev, g, outs)
+        torch.cuda.synchronize()
+        want = [pack_ref(h, g) for h in host]
+        for i, (o, w) in enumerate(zip(outs, want)):
+            assert np.array_equal(dev_to_bits(o), w), f"pack_multi tensor {i} group {g}"
+        canary_bits = [np.full((T, H, D), 0x7FA5 if dtype == "bf16" else 0x7FC0A5A5, dtype=host[0][0].dtype)
+                       for H in heads]
+        canary = [[bits_to_dev(c.copy()) for _ in range(P)] for c in canary_bits]
+        uly.ulysses_unpack_multi(outs, g, canary)
+        torch.cuda.synchronize()
+        for i in range(len(heads)):
+            want_sh = unpack_ref(want[i], [canary_bits[i]] * P, g)
+            for j in range(P):
+                assert np.array_equal(dev_to_bits(canary[i][j]), want_sh[j]), f"unpack_multi tensor {i} shard {j}"
