@@ -18,6 +18,8 @@
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   attn_bwd_accumulate  the same, adding to the gradients (chunked attention)
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
+ *   ulysses_pack_heads / ulysses_unpack_heads
+ *                    the same for any run of heads (replicated kv heads)
  *   ulysses_pack_multi / ulysses_unpack_multi
  *                    the same for up to three tensors in one launch
  *   ulysses_pack_qkv / ulysses_unpack_qkv
@@ -106,6 +108,34 @@ uly_status ulysses_pack(const void* const* shards, int P, int64_t T, int H, int 
  */
 uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dtype dt,
                           int group, void* const* shards, hipStream_t stream);
+
+/*
+ * ulysses_pack_heads -- the same regrouping for any run of heads:
+ *
+ *   out[j*T + t][h][:] = shards[j][t][head0 + h][:]      j < P, t < T, h < nheads
+ *
+ * With head0 = group*H/P and nheads = H/P it is ulysses_pack. Its other use
+ * is a tensor with fewer heads than ranks (Hkv < P): the pages do not cover
+ * that case; here the key/value heads are then replicated, rank g (query
+ * heads [g*Hq/P, (g+1)*Hq/P)) gathering the one kv head those query heads
+ * read, head0 = floor(g * Hkv / P), nheads = 1 (requires P % Hkv == 0). The
+ * backward's dK/dV of such a head is then a sum over the P/Hkv ranks sharing
+ * it, a reduction across ranks that this library does not perform.
+ * shards : host array of P device pointers to [T][H][D] tensors (read).
+ * out    : device [P*T][nheads][D] (written in full).
+ * P in [1, ULY_MAX_P]; T >= 1; 1 <= nheads and 0 <= head0 <= H - nheads;
+ * D in {64, 128}. Bit-exact; errors as ulysses_pack.
+ */
+uly_status ulysses_pack_heads(const void* const* shards, int P, int64_t T, int H, int D, uly_dtype dt,
+                              int head0, int nheads, void* out, hipStream_t stream);
+
+/*
+ * ulysses_unpack_heads -- the inverse of ulysses_pack_heads:
+ *   shards[j][t][head0 + h][:] = in[j*T + t][h][:]
+ * Every other head is left untouched. Same preconditions.
+ */
+uly_status ulysses_unpack_heads(const void* in, int P, int64_t T, int H, int D, uly_dtype dt, int head0,
+                                int nheads, void* const* shards, hipStream_t stream);
 
 /*
  * ulysses_pack_multi -- ulysses_pack of up to three tensors in one launch,

@@ -12,6 +12,10 @@ What it computes (plain numpy, fp64 for all floating point):
                           sequence for a subset of heads; "Ulysses Sequence
                           Parallelism ...", the "All-to-All Communication" step:
                           a second all-to-all reverses it)
+  pack_heads_ref / unpack_heads_ref
+                          the same for any run of heads, e.g. the replicated
+                          kv head of a rank when there are fewer kv heads than
+                          ranks (replicated_kv_head)
   pack_qkv_ref / unpack_qkv_ref
                           the same redistributions for a fused QKV projection
                           output (query, key, value heads of a token side by
@@ -35,8 +39,11 @@ from .ref import (  # noqa: F401
     doc_tables,
     f32_bits_to_f64,
     merge_ref,
+    pack_heads_ref,
     pack_qkv_ref,
     pack_ref,
+    replicated_kv_head,
+    unpack_heads_ref,
     unpack_qkv_ref,
     unpack_ref,
 )

@@ -125,6 +125,75 @@ def unpack_ref(packed: np.ndarray, shards, group: int, tokens=None):
     return [x.reshape(T, H, D) for x in out]
 
 
+def pack_heads_ref(shards, head0: int, nheads: int) -> np.ndarray:
+    """The redistribution for any run of heads [head0, head0 + nheads):
+
+        out[n, h, d] = shard_j[t, head0 + h, d],  n = j*T + t.
+
+    With head0 = group*H/P and nheads = H/P this is pack_ref. With fewer
+    key/value heads than ranks the pages say nothing; the reading taken is
+    that kv heads are replicated and rank g gathers the one its query heads
+    use (replicated_kv_head)."""
+    P, T, H, D = _check_shards_any(shards)
+    if not (nheads >= 1 and 0 <= head0 <= H - nheads):
+        raise ValueError("head run out of range")
+    o = np.arange(P * T * nheads * D, dtype=np.int64)
+    d = o % D
+    h = (o // D) % nheads
+    n = o // (nheads * D)
+    j, t = n // T, n % T
+    src = (t * H + head0 + h) * D + d
+    out = np.empty(o.size, dtype=shards[0].dtype)
+    flats = [s.reshape(-1) for s in shards]
+    for jj in range(P):
+        sel = j == jj
+        out[sel] = flats[jj][src[sel]]
+    return out.reshape(P * T, nheads, D)
+
+
+def unpack_heads_ref(packed: np.ndarray, shards, head0: int, nheads: int):
+    """Inverse of pack_heads_ref: shard_j[t, head0 + h, d] = packed[j*T + t,
+    h, d]; other heads keep the values in `shards` (new arrays returned)."""
+    P, T, H, D = _check_shards_any(shards)
+    if packed.shape != (P * T, nheads, D) or not (nheads >= 1 and 0 <= head0 <= H - nheads):
+        raise ValueError("shape or head run mismatch")
+    out = [s.copy().reshape(-1) for s in shards]
+    o = np.arange(P * T * nheads * D, dtype=np.int64)
+    d = o % D
+    h = (o // D) % nheads
+    n = o // (nheads * D)
+    j, t = n // T, n % T
+    dst = (t * H + head0 + h) * D + d
+    flat_in = packed.reshape(-1)
+    for jj in range(P):
+        sel = j == jj
+        out[jj][dst[sel]] = flat_in[o[sel]]
+    return [x.reshape(T, H, D) for x in out]
+
+
+def replicated_kv_head(g: int, P: int, Hq: int, Hkv: int) -> int:
+    """The kv head rank g needs when Hkv < P: its query heads
+    [g*Hq/P, (g+1)*Hq/P) all read kv head floor(h / (Hq/Hkv)) (consecutive
+    query heads share a kv head), which is floor(g * Hkv / P) when P is a
+    multiple of Hkv."""
+    if Hq % P or P % Hkv or Hq % Hkv:
+        raise ValueError("needs P | Hq, Hkv | P and Hkv | Hq")
+    heads = {h // (Hq // Hkv) for h in range(g * (Hq // P), (g + 1) * (Hq // P))}
+    assert len(heads) == 1
+    return heads.pop()
+
+
+def _check_shards_any(shards):
+    P = len(shards)
+    if P < 1:
+        raise ValueError("need at least one shard")
+    T, H, D = shards[0].shape
+    for s in shards:
+        if s.shape != (T, H, D) or s.dtype != shards[0].dtype:
+            raise ValueError("shards must share shape and dtype")
+    return P, T, H, D
+
+
 def _qkv_sections(shards, Hq: int, Hkv: int, group: int):
     P = len(shards)
     if P < 1:

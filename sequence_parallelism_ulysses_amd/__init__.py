@@ -27,9 +27,11 @@ from ._lib import (  # noqa: F401
     lib_path,
     uly_check_cu_seqlens,
     ulysses_pack,
+    ulysses_pack_heads,
     ulysses_pack_multi,
     ulysses_pack_qkv,
     ulysses_unpack,
+    ulysses_unpack_heads,
     ulysses_unpack_multi,
     ulysses_unpack_qkv,
 )

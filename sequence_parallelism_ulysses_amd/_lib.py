@@ -26,6 +26,8 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "ulysses_pack": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
+    "ulysses_pack_heads": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "ulysses_unpack_heads": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
     "ulysses_pack_multi": (_i32, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, _i64, _i32, _i32, _i32,
                                    ctypes.POINTER(_vp), _vp]),
     "ulysses_unpack_multi": (_i32, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, _i64, _i32, _i32, _i32,
@@ -151,6 +153,30 @@ def ulysses_unpack(inp, group: int, shards: Sequence, stream=None) -> None:
         _dev(inp, (P * T, H // P, D), dt, "inp")
     _raise(lib().ulysses_unpack(ctypes.c_void_p(inp.data_ptr()), P, T, H, D, _dtype_code(shards[0]), group,
                                 ptrs, _stream(stream)))
+
+
+def ulysses_pack_heads(shards: Sequence, head0: int, nheads: int, out, stream=None) -> None:
+    """out[j*T + t, h] = shards[j][t, head0 + h] (see include/ulysses.h)."""
+    P = len(shards)
+    T, H, D = shards[0].shape
+    dt = shards[0].dtype
+    ptrs = (ctypes.c_void_p * P)(*[_dev(s, (T, H, D), dt, f"shards[{j}]").value for j, s in enumerate(shards)])
+    if nheads >= 1:
+        _dev(out, (P * T, nheads, D), dt, "out")
+    _raise(lib().ulysses_pack_heads(ptrs, P, T, H, D, _dtype_code(shards[0]), head0, nheads,
+                                    ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+
+
+def ulysses_unpack_heads(inp, head0: int, nheads: int, shards: Sequence, stream=None) -> None:
+    """shards[j][t, head0 + h] = inp[j*T + t, h]; other heads untouched."""
+    P = len(shards)
+    T, H, D = shards[0].shape
+    dt = shards[0].dtype
+    ptrs = (ctypes.c_void_p * P)(*[_dev(s, (T, H, D), dt, f"shards[{j}]").value for j, s in enumerate(shards)])
+    if nheads >= 1:
+        _dev(inp, (P * T, nheads, D), dt, "inp")
+    _raise(lib().ulysses_unpack_heads(ctypes.c_void_p(inp.data_ptr()), P, T, H, D, _dtype_code(shards[0]), head0,
+                                      nheads, ptrs, _stream(stream)))
 
 
 def _multi(tensors, packed, name):

@@ -59,6 +59,28 @@ uly_status check_permute(const char* fn, int P, int64_t T, int H, int D, int dt,
   return ULY_OK;
 }
 
+// Any run of heads [head0, head0 + nheads) of every shard token.
+uly_status check_heads(const char* fn, int P, int64_t T, int H, int D, int dt, int head0, int nheads,
+                       uly::PermuteDesc* out) {
+  CHECK(P >= 1 && P <= ULY_MAX_P, ULY_ERR_INVALID_ARG, "%s: P=%d must be in [1, %d]", fn, P, ULY_MAX_P);
+  CHECK(T >= 1, ULY_ERR_INVALID_ARG, "%s: T=%lld must be >= 1", fn, (long long)T);
+  CHECK(H >= 1 && H <= (1 << 20), ULY_ERR_INVALID_ARG, "%s: H=%d must be in [1, 2^20]", fn, H);
+  CHECK(D == 64 || D == 128, ULY_ERR_INVALID_ARG, "%s: D=%d must be 64 or 128", fn, D);
+  CHECK(valid_dtype(dt), ULY_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
+  CHECK(nheads >= 1 && head0 >= 0 && head0 <= H - nheads, ULY_ERR_INVALID_ARG,
+        "%s: heads [%d, %d + %d) must lie in [0, H=%d)", fn, head0, head0, nheads, H);
+  const int64_t e = elem_bytes(static_cast<uly_dtype>(dt));
+  out->P = P;
+  out->T = T;
+  out->nseg = 1;
+  out->row_bytes[0] = int64_t(H) * D * e;
+  out->seg_bytes[0] = int64_t(nheads) * D * e;
+  out->head_offset[0] = int64_t(head0) * D * e;
+  CHECK(T * (out->seg_bytes[0] / 16) < (int64_t(1) << 31), ULY_ERR_UNSUPPORTED,
+        "%s: one shard's heads (%lld bytes) exceed 32 GiB", fn, (long long)(T * out->seg_bytes[0]));
+  return ULY_OK;
+}
+
 // A fused QKV shard token holds Hq query heads, then Hkv key heads, then Hkv
 // value heads; the group's slice of each section is one segment.
 uly_status check_permute_qkv(const char* fn, int P, int64_t T, int Hq, int Hkv, int D, int dt, int group,
@@ -160,6 +182,38 @@ uly_status ulysses_unpack(const void* in, int P, int64_t T, int H, int D, uly_dt
   const void* const ins[1] = {in};
   void* const* sh[1] = {shards};
   return from_hip(uly::launch_unpack(ins, sh, d, stream), "ulysses_unpack");
+}
+
+uly_status ulysses_pack_heads(const void* const* shards, int P, int64_t T, int H, int D, uly_dtype dt, int head0,
+                              int nheads, void* out, hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_heads("ulysses_pack_heads", P, T, H, D, dt, head0, nheads, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr, ULY_ERR_INVALID_ARG, "ulysses_pack_heads: shards is NULL");
+  CHECK(out != nullptr && aligned16(out), ULY_ERR_INVALID_ARG,
+        "ulysses_pack_heads: out is NULL or not 16-byte aligned");
+  for (int j = 0; j < P; ++j)
+    CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
+          "ulysses_pack_heads: shards[%d] is NULL or not 16-byte aligned", j);
+  void* const outs[1] = {out};
+  const void* const* sh[1] = {shards};
+  return from_hip(uly::launch_pack(sh, outs, d, stream), "ulysses_pack_heads");
+}
+
+uly_status ulysses_unpack_heads(const void* in, int P, int64_t T, int H, int D, uly_dtype dt, int head0, int nheads,
+                                void* const* shards, hipStream_t stream) {
+  uly::PermuteDesc d;
+  uly_status s = check_heads("ulysses_unpack_heads", P, T, H, D, dt, head0, nheads, &d);
+  if (s != ULY_OK) return s;
+  CHECK(shards != nullptr, ULY_ERR_INVALID_ARG, "ulysses_unpack_heads: shards is NULL");
+  CHECK(in != nullptr && aligned16(in), ULY_ERR_INVALID_ARG,
+        "ulysses_unpack_heads: in is NULL or not 16-byte aligned");
+  for (int j = 0; j < P; ++j)
+    CHECK(shards[j] != nullptr && aligned16(shards[j]), ULY_ERR_INVALID_ARG,
+          "ulysses_unpack_heads: shards[%d] is NULL or not 16-byte aligned", j);
+  const void* const ins[1] = {in};
+  void* const* sh[1] = {shards};
+  return from_hip(uly::launch_unpack(ins, sh, d, stream), "ulysses_unpack_heads");
 }
 
 uly_status ulysses_pack_qkv(const void* const* shards, int P, int64_t T, int Hq, int Hkv, int D,

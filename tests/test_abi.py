@@ -29,8 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_bwd", "attn_bwd_accumulate", "attn_bwd_workspace_size", "attn_fwd", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
-        "ulysses_pack", "ulysses_pack_multi", "ulysses_pack_qkv", "ulysses_unpack", "ulysses_unpack_multi",
-        "ulysses_unpack_qkv"])
+        "ulysses_pack", "ulysses_pack_heads", "ulysses_pack_multi", "ulysses_pack_qkv", "ulysses_unpack",
+        "ulysses_unpack_heads", "ulysses_unpack_multi", "ulysses_unpack_qkv"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -178,6 +178,26 @@ def _multi(fn="ulysses_pack_multi", **kw):
 ])
 def test_multi_rejects(fn, kw, status, needle):
     assert _multi(fn, **kw) == status
+    assert needle in uly.last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(h0=-1), uly.ULY_ERR_INVALID_ARG, "heads [-1"),
+    (dict(h0=7, nh=2), uly.ULY_ERR_INVALID_ARG, "heads [7"),
+    (dict(nh=0), uly.ULY_ERR_INVALID_ARG, "heads [0"),
+    (dict(D=32), uly.ULY_ERR_INVALID_ARG, "D=32"),
+    (dict(P=0), uly.ULY_ERR_INVALID_ARG, "P=0"),
+    (dict(out=FAKE + 4), uly.ULY_ERR_INVALID_ARG, "not 16-byte"),
+])
+def test_heads_rejects(kw, status, needle):
+    a = dict(P=4, T=256, H=8, D=64, dt=uly.ULY_BF16, h0=0, nh=1, out=FAKE)
+    a.update(kw)
+    sh = _ptrs(max(a["P"], 1))
+    assert uly.lib().ulysses_pack_heads(sh, a["P"], a["T"], a["H"], a["D"], a["dt"], a["h0"], a["nh"], a["out"],
+                                        None) == status
+    assert needle in uly.last_error()
+    assert uly.lib().ulysses_unpack_heads(a["out"], a["P"], a["T"], a["H"], a["D"], a["dt"], a["h0"], a["nh"], sh,
+                                          None) == status
     assert needle in uly.last_error()
 
 

@@ -5,7 +5,8 @@ import torch
 
 import sequence_parallelism_ulysses_amd as uly
 import synthetic as syn
-from oracle import pack_qkv_ref, pack_ref, unpack_qkv_ref, unpack_ref
+from oracle import (pack_heads_ref, pack_qkv_ref, pack_ref, replicated_kv_head, unpack_heads_ref,
+                    unpack_qkv_ref, unpack_ref)
 from harness import DEV, bits_to_dev, dev_to_bits
 
 pytestmark = pytest.mark.gpu
@@ -215,3 +216,34 @@ def test_pack_unpack_multi_bit_exact(P, T, heads, D, dtype):
             want_sh = unpack_ref(want[i], [canary_bits[i]] * P, g)
             for j in range(P):
                 assert np.array_equal(dev_to_bits(canary[i][j]), want_sh[j]), f"unpack_multi tensor {i} shard {j}"
+
+
+HEADS_CASES = [
+    # (P, T, H, D, dtype, [(head0, nheads), ...])
+    (16, 2048, 8, 128, "bf16", [(replicated_kv_head(g, 16, 32, 8), 1) for g in (0, 1, 2, 7, 15)]),  # kv heads replicated
+    (3, 37, 12, 64, "bf16", [(3, 5), (0, 12), (11, 1)]),     # any run of heads, ragged T
+    (4, 256, 8, 64, "f32", [(2, 2), (5, 3)]),                 # fp32
+    (64, 2, 4, 128, "bf16", [(1, 2)]),                        # more ranks than heads
+]
+
+
+@pytest.mark.parametrize("P,T,H,D,dtype,runs", HEADS_CASES)
+def test_pack_unpack_heads_bit_exact(P, T, H, D, dtype, runs):
+    """Head runs (including the replicated kv head of a rank when there are
+    fewer kv heads than ranks) against the oracle bit for bit; the inverse
+    into canary-filled shards."""
+    host = _host_shards(P, T, H, D, dtype, seed=13 * P + T)
+    dev = [bits_to_dev(s) for s in host]
+    for h0, nh in runs:
+        out = torch.empty((P * T, nh, D), dtype=dev[0].dtype, device=DEV)
+        uly.ulysses_pack_heads(dev, h0, nh, out)
+        torch.cuda.synchronize()
+        want = pack_heads_ref(host, h0, nh)
+        assert np.array_equal(dev_to_bits(out), want), f"pack_heads [{h0}, +{nh})"
+        canary_bits = np.full((T, H, D), 0x7FA5 if dtype == "bf16" else 0x7FC0A5A5, dtype=host[0].dtype)
+        canary = [bits_to_dev(canary_bits.copy()) for _ in range(P)]
+        uly.ulysses_unpack_heads(out, h0, nh, canary)
+        torch.cuda.synchronize()
+        want_sh = unpack_heads_ref(want, [canary_bits] * P, h0, nh)
+        for j in range(P):
+            assert np.array_equal(dev_to_bits(canary[j]), want_sh[j]), f"unpack_heads shard {j}"

@@ -18,8 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attn_ref, bf16_bits_to_f64, doc_tables, f32_bits_to_f64, merge_ref, pack_qkv_ref, pack_ref,
-                    unpack_qkv_ref, unpack_ref)
+from oracle import (attn_ref, bf16_bits_to_f64, doc_tables, f32_bits_to_f64, merge_ref, pack_heads_ref, pack_qkv_ref,
+                    pack_ref, replicated_kv_head, unpack_heads_ref, unpack_qkv_ref, unpack_ref)
 from synthetic import cu_from_lengths
 
 
@@ -111,6 +111,56 @@ def test_pack_token_subset():
         for t in range(T):
             if (j, t) not in written:
                 assert not a[j][t].any()
+
+
+# ------------------------------------------------------------- head-run pack/unpack
+@pytest.mark.parametrize("P,T,H,D,h0,nh", [(2, 3, 4, 2, 1, 2), (4, 2, 2, 3, 1, 1), (1, 4, 5, 2, 0, 5), (3, 2, 6, 1, 5, 1)])
+def test_pack_heads_matches_python_loops_and_slicing(P, T, H, D, h0, nh):
+    """Brute force over (shard, token, head, dim), and numpy concatenate +
+    slice. Catches an offset applied per group instead of per head."""
+    sh = _shards(P, T, H, D, seed=51)
+    want = np.zeros((P * T, nh, D), dtype=np.uint16)
+    for j in range(P):
+        for t in range(T):
+            for h in range(nh):
+                for d in range(D):
+                    want[j * T + t, h, d] = sh[j][t, h0 + h, d]
+    got = pack_heads_ref(sh, h0, nh)
+    assert np.array_equal(got, want)
+    assert np.array_equal(got, np.concatenate(sh, axis=0)[:, h0:h0 + nh])
+
+
+def test_pack_heads_is_pack_for_a_group_and_inverts():
+    P, T, H, D = 4, 5, 8, 3
+    sh = _shards(P, T, H, D, seed=52)
+    for g in range(P):
+        packed = pack_heads_ref(sh, g * 2, 2)
+        assert np.array_equal(packed, pack_ref(sh, g))
+        canary = [np.full_like(s, 0xBEEF) for s in sh]
+        for o, s in zip(unpack_heads_ref(packed, canary, g * 2, 2), sh):
+            assert np.all(o[:, :g * 2] == 0xBEEF) and np.all(o[:, g * 2 + 2:] == 0xBEEF)
+            assert np.array_equal(o[:, g * 2:g * 2 + 2], s[:, g * 2:g * 2 + 2])
+
+
+def test_replicated_kv_head_attention_is_a_slice_of_all_heads():
+    """Fewer kv heads than ranks (Hq = 8, Hkv = 2, P = 4): rank g's query
+    heads with the one kv head it gathers give exactly the slice of
+    attention over all heads (GQA with consecutive query heads per kv
+    head). Catches a replicated head taken as g % Hkv instead of g*Hkv/P."""
+    r = _rng(53)
+    P, T, Hq, Hkv, D = 4, 3, 8, 2, 4
+    N = P * T
+    qs = [r.normal(size=(T, Hq, D)) for _ in range(P)]
+    ks = [r.normal(size=(T, Hkv, D)) for _ in range(P)]
+    vs = [r.normal(size=(T, Hkv, D)) for _ in range(P)]
+    full = attn_ref(np.concatenate(qs), np.concatenate(ks), np.concatenate(vs), 0.5, workers=1)
+    assert [replicated_kv_head(g, P, Hq, Hkv) for g in range(P)] == [0, 0, 1, 1]
+    for g in range(P):
+        kv = replicated_kv_head(g, P, Hq, Hkv)
+        q = pack_ref(qs, g)
+        k, v = pack_heads_ref(ks, kv, 1), pack_heads_ref(vs, kv, 1)
+        res = attn_ref(q, k, v, 0.5, workers=1)
+        assert np.allclose(res["o"], full["o"][:, g * 2:(g + 1) * 2], atol=1e-13)
 
 
 # ------------------------------------------------------- fused QKV pack/unpack
