@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------
 // bf16 kernels on row-major LDS tiles (lds_tile.hpp): every tile is copied by
-// buffer_load ... lds into a three-stage ring, and the transposed operands
+// buffer_load ... lds into a four-stage ring (three tiles ahead), and the transposed operands
 // (Q^T, dO^T, K^T) are read with ds_read_b64_tr_b16 instead of being stored
 // twice. One barrier per tile; a stage is refilled only after the tile's LDS
 // reads (the compiler waits for in-flight LDS copies before transposed reads).
@@ -544,7 +544,7 @@ struct DqBf {
   static constexpr int DB = D / 32;
   static constexpr int TB = TileFmt<D>::kBytes;
   static constexpr int STAGE = 2 * TB;  // K, V
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = 4;
   static constexpr int LOADS = 2 * tile_loads<D, kThreads>();
 };
 
@@ -606,9 +606,10 @@ void dq_bf16_kernel(BwdParams p) {
   };
   issue(t0);
   if (t0 + 1 <= t1) issue(t0 + 1);
+  if (t0 + 2 <= t1) issue(t0 + 2);
 
   for (int t = t0; t <= t1; ++t) {
-    if (t + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
+    if (t + 2 <= t1) wait_vmcnt<2 * C::LOADS>(); else if (t + 1 <= t1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
     __syncthreads();
     const int kv0 = t * BT;
     const lds_char* kr = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
@@ -644,7 +645,7 @@ void dq_bf16_kernel(BwdParams p) {
         for (int db = 0; db < C::DB; ++db) dqt[db] = mfma(frag_cols_tr<D>(kr, st2 * 16, db * 32, lane), sf, dqt[db]);
       }
     }
-    if (t + 2 <= t1) issue(t + 2);
+    if (t + 3 <= t1) issue(t + 3);
   }
 
   if (active && q_ok) {
