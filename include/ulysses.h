@@ -254,8 +254,11 @@ uly_status attn_merge(const void* const* o_parts, const float* const* lse_parts,
                       int hq, int D, uly_dtype dt, void* o, float* lse, hipStream_t stream);
 
 /*
- * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
- * these sizes (currently the per-row delta_i = dO_i . O_i, float32 [hq][N]).
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd (and
+ * attn_bwd_accumulate) needs for these sizes: the per-row delta_i =
+ * dO_i . O_i and lse_i * log2(e) (float32 [hq][N] each) and the float32
+ * partial dK/dV sums of the workgroups that share a key block (2 x 4 x
+ * N x hk x D floats).
  */
 uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype dt,
                                    size_t* bytes);
