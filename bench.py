@@ -81,10 +81,13 @@ def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
         R = min(cfg.N, int(R * max(1.5, min(8.0, budget_s / max(dt, 1e-3)))))
         dt, pairs = run(R)
     flops = 14 * cfg.D * cfg.hq * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+    rate = flops / dt
+    full = 14 * cfg.D * cfg.hq * causal_pairs(cfg.N, cu)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"fp64 numpy oracle, forward+backward of the last {R} query rows x {cfg.hq} q heads "
-                      f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}"}
+                      f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}",
+            "full_step_seconds_extrapolated": round(full / rate, 1)}
 
 
 # The sources of the attn_bwd call's kernels (and what they include).
