@@ -247,3 +247,39 @@ def test_pack_unpack_heads_bit_exact(P, T, H, D, dtype, runs):
         want_sh = unpack_heads_ref(want, [canary_bits] * P, h0, nh)
         for j in range(P):
             assert np.array_equal(dev_to_bits(canary[j]), want_sh[j]), f"unpack_heads shard {j}"
+
+
+@pytest.mark.parametrize("T", [16384, 131072])
+def test_pack_unpack_multi_full_size_sampled(T):
+    """The step's regrouping of Q, K, V (32, 8, 8 heads over 8 ranks) in one
+    launch at 128k and 1M tokens (the all-shards Q of the latter holds 2^32
+    elements): the last group, checked on sampled tokens of every shard
+    against the oracle; then the inverse into zeroed heads."""
+    P, D, g = 8, 128, 7
+    heads = (32, 8, 8)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(T + 17)
+    dev = [[torch.randint(-32768, 32767, (T, H, D), dtype=torch.int16, device=DEV, generator=gen).view(torch.bfloat16)
+            for _ in range(P)] for H in heads]
+    outs = [torch.empty((P * T, H // P, D), dtype=torch.bfloat16, device=DEV) for H in heads]
+    uly.ulysses_pack_multi(dev, g, outs)
+    torch.cuda.synchronize()
+    ts = np.array([0, 1, 4095, T // 2, T - 2, T - 1])
+    idx = torch.from_numpy(ts).to(DEV)
+    rows = torch.from_numpy(np.concatenate([j * T + ts for j in range(P)])).to(DEV)
+    minis = []
+    for i, H in enumerate(heads):
+        mini = [dev_to_bits(s[idx]) for s in dev[i]]
+        minis.append(mini)
+        assert np.array_equal(dev_to_bits(outs[i][rows]), pack_ref(mini, g)), f"tensor {i}"
+    hh = [H // P for H in heads]
+    for i in range(len(heads)):
+        for s in dev[i]:
+            s.view(torch.int16)[:, g * hh[i]:(g + 1) * hh[i], :] = 0
+    uly.ulysses_unpack_multi(outs, g, dev)
+    torch.cuda.synchronize()
+    for i in range(len(heads)):
+        for j in range(P):
+            assert np.array_equal(dev_to_bits(dev[i][j][idx]), minis[i][j]), f"unpack tensor {i} shard {j}"
+    del dev, outs
+    torch.cuda.empty_cache()
