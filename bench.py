@@ -168,6 +168,30 @@ def fused_qkv_rates(uly, cfg, reps: int) -> dict:
     return res
 
 
+def fwd_from_shards_rate(uly, cfg, shards, cu_dev, fwd_flop: int, pack_fwd_ms: float, reps: int) -> dict:
+    """attn_fwd_from_shards on the workload's sequence-sharded Q/K/V (no pack
+    of Q, K, V before the forward), beside the step's pack + attn_fwd."""
+    import torch
+    dev = shards["q"][0].device
+    o = torch.empty((cfg.N, cfg.hq, cfg.D), dtype=shards["q"][0].dtype, device=dev)
+    lse = torch.empty((cfg.hq, cfg.N), dtype=torch.float32, device=dev)
+
+    def run():
+        uly.attn_fwd_from_shards(shards["q"], shards["k"], shards["v"], cfg.group, o, lse, cfg.scale, cu_dev)
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tf = fwd_flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "pack_qkv_plus_attn_fwd_ms": round(pack_fwd_ms, 4)}
+
+
 def chunked_rates(uly, cfg, qg, kg, vg, dog, fwd_flop: int, bwd_flop: int, call_ms: dict, reps: int) -> dict:
     """Attention computed ring-style on this GPU: the sequence in P chunks;
     forward = query chunk i against key chunks c < i (attn_fwd, causal = 0)
@@ -385,6 +409,9 @@ def main() -> int:
     }
     if not args.no_side_legs:
         line["fused_qkv"] = fused_qkv_rates(uly, cfg, args.steps)
+        if cfg.T % 64 == 0:
+            line["fwd_from_shards"] = fwd_from_shards_rate(uly, cfg, shards, cu_dev, fwd_flop,
+                                                           call_ms["pack_qkv"] + call_ms["attn_fwd"], args.steps)
     if cu is None and not args.no_side_legs:
         line["chunked"] = chunked_rates(uly, cfg, qg, kg, vg, dog, fwd_flop, bwd_flop, call_ms,
                                         max(3, args.steps // 4))

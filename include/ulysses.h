@@ -14,6 +14,7 @@
  *   ulysses_pack     sequence-sharded -> head-sharded layout for one head group
  *   attn_fwd         causal or document-masked (optionally packed-document) GQA
  *                    attention forward
+ *   attn_fwd_from_shards  the same, reading sequence-sharded Q/K/V in place
  *   attn_merge       combine attention results over disjoint key chunks (LSE merge)
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   attn_bwd_accumulate  the same, adding to the gradients (chunked attention)
@@ -230,6 +231,26 @@ uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float*
                     int64_t N, int hq, int hk, int D, uly_dtype dt,
                     const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                     hipStream_t stream);
+
+/*
+ * attn_fwd_from_shards -- attn_fwd for head group `group` reading Q, K and V
+ * in place from the sequence-sharded tensors, so that on one GPU their pack
+ * disappears: the kernels' tile loads take token n of the group from shard
+ * n / T, row n % T, heads [group*Hq/P, ...) and [group*Hkv/P, ...). Same
+ * result, bit for bit, as ulysses_pack of Q, K and V followed by attn_fwd.
+ *
+ * q_shards : host array of P device pointers to [T][Hq][D]; k_shards,
+ *            v_shards : likewise [T][Hkv][D].
+ * o        : device [P*T][Hq/P][D] (head-group layout, as attn_fwd writes it).
+ * lse      : device float32 [Hq/P][P*T].
+ * Requires dt == ULY_BF16 and T % 64 == 0 (else ULY_ERR_UNSUPPORTED),
+ * Hq % P == 0, Hkv % P == 0, 0 <= group < P; other arguments and errors as
+ * attn_fwd with N = P*T, hq = Hq/P, hk = Hkv/P.
+ */
+uly_status attn_fwd_from_shards(const void* const* q_shards, const void* const* k_shards,
+                                const void* const* v_shards, int P, int64_t T, int Hq, int Hkv, int D,
+                                uly_dtype dt, int group, void* o, float* lse, const int32_t* cu_seqlens,
+                                int ndocs, float softmax_scale, int causal, hipStream_t stream);
 
 /*
  * attn_merge -- combine attention results computed over disjoint sets of

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_accumulate,
     attn_bwd_workspace_size,
     attn_fwd,
+    attn_fwd_from_shards,
     attn_merge,
     last_error,
     lib,

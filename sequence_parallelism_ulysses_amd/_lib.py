@@ -37,6 +37,8 @@ SIGNATURES = {
     "ulysses_unpack_qkv": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32,
                                    ctypes.POINTER(_vp), _vp]),
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32, _f32, _i32, _vp]),
+    "attn_fwd_from_shards": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i64, _i32,
+                                     _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _i32, _vp]),
     "attn_merge": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
@@ -260,6 +262,30 @@ def attn_fwd(q, k, v, o, lse, softmax_scale: float, cu_seqlens=None, causal: int
     cu, nd = _cu(cu_seqlens, N)
     _raise(lib().attn_fwd(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
                           _stream(stream)))
+
+
+def attn_fwd_from_shards(q_shards: Sequence, k_shards: Sequence, v_shards: Sequence, group: int, o, lse,
+                         softmax_scale: float, cu_seqlens=None, causal: int = 1, stream=None) -> None:
+    """attn_fwd for head group `group`, reading the sequence-sharded Q/K/V in
+    place (see include/ulysses.h)."""
+    import torch
+    P = len(q_shards)
+    if len(k_shards) != P or len(v_shards) != P:
+        raise ValueError("q, k and v need the same number of shards")
+    T, Hq, D = q_shards[0].shape
+    Hkv = k_shards[0].shape[1]
+    dt = q_shards[0].dtype
+
+    def arr(shards, H, name):
+        return (ctypes.c_void_p * P)(*[_dev(s, (T, H, D), dt, f"{name}[{j}]").value for j, s in enumerate(shards)])
+    qa, ka, va = arr(q_shards, Hq, "q_shards"), arr(k_shards, Hkv, "k_shards"), arr(v_shards, Hkv, "v_shards")
+    if Hq % P == 0:
+        _dev(o, (P * T, Hq // P, D), dt, "o")
+        _dev(lse, (Hq // P, P * T), torch.float32, "lse")
+    cu, nd = _cu(cu_seqlens, P * T)
+    _raise(lib().attn_fwd_from_shards(qa, ka, va, P, T, Hq, Hkv, D, _dtype_code(q_shards[0]), group,
+                                      ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse.data_ptr()), cu, nd,
+                                      float(softmax_scale), int(causal), _stream(stream)))
 
 
 def attn_merge(o_parts: Sequence, lse_parts: Sequence, o, lse, stream=None) -> None:

@@ -334,6 +334,34 @@ uly_status attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   return from_hip(uly::launch_attn_fwd(q, k, v, o, lse, d, stream), "attn_fwd");
 }
 
+uly_status attn_fwd_from_shards(const void* const* q_shards, const void* const* k_shards,
+                                const void* const* v_shards, int P, int64_t T, int Hq, int Hkv, int D, uly_dtype dt,
+                                int group, void* o, float* lse, const int32_t* cu_seqlens, int ndocs,
+                                float softmax_scale, int causal, hipStream_t stream) {
+  const char* fn = "attn_fwd_from_shards";
+  CHECK(P >= 1 && P <= ULY_MAX_P, ULY_ERR_INVALID_ARG, "%s: P=%d must be in [1, %d]", fn, P, ULY_MAX_P);
+  CHECK(T >= 1 && T <= (int64_t(1) << 30), ULY_ERR_INVALID_ARG, "%s: T=%lld must be in [1, 2^30]", fn, (long long)T);
+  CHECK(Hq >= 1 && Hq % P == 0 && Hkv >= 1 && Hkv % P == 0, ULY_ERR_INVALID_ARG,
+        "%s: Hq=%d and Hkv=%d must be positive multiples of P=%d", fn, Hq, Hkv, P);
+  CHECK(Hq <= 4096 && Hkv <= 4096, ULY_ERR_INVALID_ARG, "%s: Hq=%d, Hkv=%d too large", fn, Hq, Hkv);
+  CHECK(group >= 0 && group < P, ULY_ERR_INVALID_ARG, "%s: group=%d must be in [0, P=%d)", fn, group, P);
+  uly::AttnDesc d;
+  uly_status s = check_attn(fn, int64_t(P) * T, Hq / P, Hkv / P, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
+  if (s != ULY_OK) return s;
+  CHECK(dt == ULY_BF16, ULY_ERR_UNSUPPORTED, "%s: only bf16 inputs are read in place", fn);
+  CHECK(T % 64 == 0, ULY_ERR_UNSUPPORTED, "%s: T=%lld must be a multiple of 64", fn, (long long)T);
+  CHECK(q_shards != nullptr && k_shards != nullptr && v_shards != nullptr, ULY_ERR_INVALID_ARG,
+        "%s: a shard array is NULL", fn);
+  for (int j = 0; j < P; ++j)
+    CHECK(q_shards[j] != nullptr && aligned16(q_shards[j]) && k_shards[j] != nullptr && aligned16(k_shards[j]) &&
+              v_shards[j] != nullptr && aligned16(v_shards[j]),
+          ULY_ERR_INVALID_ARG, "%s: shard %d of q, k or v is NULL or not 16-byte aligned", fn, j);
+  CHECK(o != nullptr && aligned16(o) && lse != nullptr && aligned16(lse), ULY_ERR_INVALID_ARG,
+        "%s: o or lse is NULL or not 16-byte aligned", fn);
+  return from_hip(uly::launch_attn_fwd_from_shards(q_shards, k_shards, v_shards, P, T, Hq, Hkv, group, o, lse, d,
+                                                   stream), fn);
+}
+
 uly_status attn_merge(const void* const* o_parts, const float* const* lse_parts, int nparts, int64_t N, int hq,
                       int D, uly_dtype dt, void* o, float* lse, hipStream_t stream) {
   CHECK(nparts >= 1 && nparts <= ULY_MAX_P, ULY_ERR_INVALID_ARG, "attn_merge: nparts=%d must be in [1, %d]", nparts,

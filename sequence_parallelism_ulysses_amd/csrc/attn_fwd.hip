@@ -55,6 +55,21 @@ struct FwdParams {
   float scale_log2;
 };
 
+// Sequence-sharded sources read in place (the bf16 kernel's shard mode): the
+// token n of a head group lives in shard n / T at row n % T, its heads after
+// q_head0 / kv_head0. With T a multiple of 64 a wave's 32 query rows and a
+// 64-key tile each lie in one shard.
+struct ShardSrc {
+  const char* q[ULY_MAX_P];
+  const char* k[ULY_MAX_P];
+  const char* v[ULY_MAX_P];
+  int T;
+  int q_row;     // bytes of one shard token of Q (all Hq heads)
+  int kv_row;    // bytes of one shard token of K or V (all Hkv heads)
+  int q_head0;   // first query head of the group in a shard token
+  int kv_head0;  // first kv head of the group
+};
+
 // The fp32 kernel: 4 waves of 32 query rows.
 template <class Tr, int D>
 struct FwdCfg {
@@ -319,9 +334,9 @@ struct FwdBf {
   static constexpr int LOADS = tile_loads<D, kCopiers>();  // per copying lane per stage
 };
 
-template <int D>
+template <int D, bool kShards>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_bf16_kernel(FwdParams p) {
+void attn_fwd_bf16_kernel(FwdParams p, ShardSrc sh) {
   using C = FwdBf<D>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::NSTAGE * C::STAGE];
   lds_char* smem = (lds_char*)smem_raw;
@@ -359,7 +374,15 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   bf16x8_t qf[C::KS];
   const int64_t q_row = int64_t(p.hq) * D * 2;
   {
-    const char* src = p.q + int64_t(my_q) * q_row + int64_t(head) * D * 2 + half * 16;
+    const char* src;
+    if constexpr (kShards) {
+      // the wave's 32 rows lie in one shard (T is a multiple of 64)
+      const int j = uniform(min(qbase, p.N - 1) / sh.T);
+      const int t = my_q - j * sh.T;
+      src = sh.q[j] + int64_t(t) * sh.q_row + int64_t(sh.q_head0 + head) * D * 2 + half * 16;
+    } else {
+      src = p.q + int64_t(my_q) * q_row + int64_t(head) * D * 2 + half * 16;
+    }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
       qf[ks] = my_q < p.N ? *reinterpret_cast<const bf16x8_t*>(src + ks * 32) : bf16x8_t{};
@@ -392,10 +415,20 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   auto issue = [&](int t, bool v_tile) {
     lds_char* st = smem + ((t - t0) % C::NSTAGE) * C::STAGE;
     const int kv0 = t * BN;
-    const uint32_t bytes = uint32_t(min(BN, p.N - kv0)) * kv_row;
-    const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
-    issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform((v_tile ? p.v : p.k) + off, bytes), kv_row,
-                                         st + (v_tile ? C::TB : 0), gtid);
+    if constexpr (kShards) {
+      // the tile's 64 keys lie in shard j (T is a multiple of 64); rows are a
+      // shard token apart, and the resource ends after the last valid row's head
+      const int j = kv0 / sh.T, r0 = kv0 - j * sh.T;
+      const char* base = (v_tile ? sh.v[j] : sh.k[j]) + int64_t(r0) * sh.kv_row + int64_t(sh.kv_head0 + kvh) * D * 2;
+      const uint32_t bytes = uint32_t(min(BN, p.N - kv0) - 1) * uint32_t(sh.kv_row) + D * 2;
+      issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform(base, bytes), uint32_t(sh.kv_row),
+                                           st + (v_tile ? C::TB : 0), gtid);
+    } else {
+      const uint32_t bytes = uint32_t(min(BN, p.N - kv0)) * kv_row;
+      const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
+      issue_tile<D, C::kCopiers, 64, true>(make_rsrc_uniform((v_tile ? p.v : p.k) + off, bytes), kv_row,
+                                           st + (v_tile ? C::TB : 0), gtid);
+    }
   };
   // tile t must have landed; this group's copies of up to two later tiles may be in flight
   auto wait_tile = [&](int t) {
@@ -531,7 +564,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 
 template <int D>
 hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnDesc& d,
-                       hipStream_t stream) {
+                       hipStream_t stream, const ShardSrc* shards = nullptr) {
   using C = FwdBf<D>;
   FwdParams p;
   p.q = static_cast<const char*>(q);
@@ -551,7 +584,10 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, flo
   p.scale_log2 = d.scale * kLog2e;
   p.causal = d.causal;
   dim3 grid(p.n_qtiles, d.hk * (p.G / p.Gw));
-  attn_fwd_bf16_kernel<D><<<grid, C::kThreads, 0, stream>>>(p);
+  if (shards)
+    attn_fwd_bf16_kernel<D, true><<<grid, C::kThreads, 0, stream>>>(p, *shards);
+  else
+    attn_fwd_bf16_kernel<D, false><<<grid, C::kThreads, 0, stream>>>(p, ShardSrc{});
   return hipGetLastError();
 }
 
@@ -582,6 +618,24 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 }
 
 }  // namespace
+
+hipError_t launch_attn_fwd_from_shards(const void* const* q_shards, const void* const* k_shards,
+                                       const void* const* v_shards, int P, int64_t T, int Hq, int Hkv, int group,
+                                       void* o, float* lse, const AttnDesc& d, hipStream_t stream) {
+  ShardSrc sh{};
+  for (int j = 0; j < P; ++j) {
+    sh.q[j] = static_cast<const char*>(q_shards[j]);
+    sh.k[j] = static_cast<const char*>(k_shards[j]);
+    sh.v[j] = static_cast<const char*>(v_shards[j]);
+  }
+  sh.T = static_cast<int>(T);
+  sh.q_row = Hq * d.D * 2;
+  sh.kv_row = Hkv * d.D * 2;
+  sh.q_head0 = group * d.hq;
+  sh.kv_head0 = group * d.hk;
+  return d.D == 128 ? launch_bf16<128>(nullptr, nullptr, nullptr, o, lse, d, stream, &sh)
+                    : launch_bf16<64>(nullptr, nullptr, nullptr, o, lse, d, stream, &sh);
+}
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const AttnDesc& d, hipStream_t stream) {

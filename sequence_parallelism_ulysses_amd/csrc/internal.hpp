@@ -44,6 +44,12 @@ struct AttnDesc {
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const AttnDesc& d, hipStream_t stream);
 
+// attn_fwd reading Q, K, V in place from P sequence-sharded tensors (bf16,
+// T a multiple of 64); d describes the head group (N = P*T, hq, hk).
+hipError_t launch_attn_fwd_from_shards(const void* const* q_shards, const void* const* k_shards,
+                                       const void* const* v_shards, int P, int64_t T, int Hq, int Hkv, int group,
+                                       void* o, float* lse, const AttnDesc& d, hipStream_t stream);
+
 // o = sum_c exp(lse_c - lse) o_c, lse = log sum_c exp(lse_c), per (row, head).
 hipError_t launch_attn_merge(const void* const* o_parts, const float* const* lse_parts, int nparts, int64_t N,
                              int hq, int D, uly_dtype dt, void* o, float* lse, hipStream_t stream);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_workspace_size", "attn_fwd", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
+        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_from_shards", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
         "ulysses_pack", "ulysses_pack_heads", "ulysses_pack_multi", "ulysses_pack_qkv", "ulysses_unpack",
         "ulysses_unpack_heads", "ulysses_unpack_multi", "ulysses_unpack_qkv"])
 
@@ -198,6 +198,34 @@ def test_heads_rejects(kw, status, needle):
     assert needle in uly.last_error()
     assert uly.lib().ulysses_unpack_heads(a["out"], a["P"], a["T"], a["H"], a["D"], a["dt"], a["h0"], a["nh"], sh,
                                           None) == status
+    assert needle in uly.last_error()
+
+
+def _fwd_sh(**kw):
+    a = dict(q=_ptrs(8), k=_ptrs(8, base=FAKE + (1 << 24)), v=_ptrs(8, base=FAKE + (2 << 24)), P=8, T=4096, Hq=32,
+             Hkv=8, D=128, dt=uly.ULY_BF16, group=0, o=FAKE + (3 << 24), lse=FAKE + (4 << 24), cu=None, nd=0,
+             scale=0.088, causal=1, stream=None)
+    a.update(kw)
+    return uly.lib().attn_fwd_from_shards(a["q"], a["k"], a["v"], a["P"], a["T"], a["Hq"], a["Hkv"], a["D"], a["dt"],
+                                          a["group"], a["o"], a["lse"], a["cu"], a["nd"], a["scale"], a["causal"],
+                                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=uly.ULY_F32), uly.ULY_ERR_UNSUPPORTED, "bf16"),
+    (dict(T=4000), uly.ULY_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(Hq=30), uly.ULY_ERR_INVALID_ARG, "Hq=30"),
+    (dict(Hkv=4), uly.ULY_ERR_INVALID_ARG, "Hkv=4"),
+    (dict(group=8), uly.ULY_ERR_INVALID_ARG, "group=8"),
+    (dict(P=0), uly.ULY_ERR_INVALID_ARG, "P=0"),
+    (dict(D=96), uly.ULY_ERR_INVALID_ARG, "D=96"),
+    (dict(causal=3), uly.ULY_ERR_INVALID_ARG, "causal=3"),
+    (dict(k=None), uly.ULY_ERR_INVALID_ARG, "NULL"),
+    (dict(v=(ctypes.c_void_p * 8)(*([FAKE] * 5 + [FAKE + 2] + [FAKE] * 2))), uly.ULY_ERR_INVALID_ARG, "shard 5"),
+    (dict(lse=FAKE + 4), uly.ULY_ERR_INVALID_ARG, "o or lse"),
+])
+def test_fwd_from_shards_rejects(kw, status, needle):
+    assert _fwd_sh(**kw) == status
     assert needle in uly.last_error()
 
 
