@@ -625,16 +625,23 @@ void dq_bf16_kernel(BwdParams p) {
           s[kb] = mfma(frag_rows<D>(kr, kb * 32 + l32, ks * 16, half), qf[ks], s[kb]);
           dp[kb] = mfma(frag_rows<D>(vr, kb * 32 + l32, ks * 16, half), df[ks], dp[kb]);
         }
+      // masked scores become -inf (their exponentials exact zeros) in a loop
+      // of their own, so the exponentials below are one straight run
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int k = kv0 + kb * 32 + acc_row(r, half);
+            if (k > my_hi || k < my_ds) s[kb][r] = -INFINITY;
+          }
+      }
       float dsv[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
-          if (need_mask) {
-            const int k = kv0 + kb * 32 + acc_row(r, half);
-            if (k > my_hi || k < my_ds) e = 0.f;
-          }
+          const float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
           dsv[kb * 16 + r] = e * (dp[kb][r] - my_dlt);
         }
       // dQ^T += K^T dS^T, K^T read transposed from the row-major K tile
