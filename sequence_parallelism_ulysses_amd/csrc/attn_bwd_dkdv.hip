@@ -61,7 +61,13 @@ void dkdv_bf16_kernel(BwdParams p) {
   const bool producer = w < 4;
   const int kvh = blockIdx.y;
   const int split = int(blockIdx.x) % p.splits;
-  const int kv0 = (int(blockIdx.x) / p.splits) * C::kKeys;  // first tiles carry the most causal work
+  // heaviest key blocks first: the first blocks of the sequence, or with a
+  // few packed documents the blocks farthest from their document's end
+  const int rank = int(blockIdx.x) / p.splits;
+  const int kblock = (p.cu != nullptr && p.causal && p.ndocs < 64)
+                         ? uniform(key_block_by_work_rank(p.cu, p.ndocs, p.N, C::kKeys, p.n_tiles, rank))
+                         : rank;
+  const int kv0 = kblock * C::kKeys;
   const int kw0 = kv0 + 32 * kb;
   const int key = kw0 + l32;
   const KeyBounds kbd(p, key, kw0);

@@ -94,12 +94,12 @@ __device__ __forceinline__ DocSpan doc_of(const int32_t* __restrict__ cu, int nd
 // those holding that key. Every lane returns the same tile. Requires
 // 1 <= ndocs <= 64 and valid cu_seqlens; without documents the order is
 // simply q = n_tiles - 1 - b.
-__device__ __forceinline__ int tile_by_work_rank(const int32_t* __restrict__ cu, int ndocs, int R, int n_tiles,
-                                                 int b) {
+// The core takes this lane's document span [c0, c1) (has_doc false: no
+// document on this lane); the spans must tile [0, n_tiles*R) or [0, N).
+__device__ __forceinline__ int tile_by_work_rank_spans(bool has_doc, int c0, int c1, int R, int n_tiles, int b) {
   const int lane = threadIdx.x & 63;
   int a = 1, e = 0, base = 0;  // lanes without a document hold an empty range
-  if (lane < ndocs) {
-    const int c0 = cu[lane], c1 = cu[lane + 1];
+  if (has_doc) {
     base = c0 / R;
     a = (c0 + R - 1) / R - base;
     e = (c1 + R - 1) / R - 1 - base;
@@ -118,13 +118,40 @@ __device__ __forceinline__ int tile_by_work_rank(const int32_t* __restrict__ cu,
     if (count_ge(mid) > b) lo = mid; else hi = mid;
   }
   const int j = b - count_ge(lo + 1);  // rank among the documents holding key lo
-  const bool has = lane < ndocs && a <= lo && lo <= e;
+  const bool has = has_doc && a <= lo && lo <= e;
   const uint64_t mask = __ballot(has);
   const int above = __popcll((mask >> lane) >> 1);  // documents after this lane's holding key lo
   const uint64_t pick = __ballot(has && above == j);
   const int d = pick ? __ffsll(static_cast<unsigned long long>(pick)) - 1 : 0;
   const int q = __shfl(base, d) + lo;
   return q < 0 ? 0 : (q >= n_tiles ? n_tiles - 1 : q);
+}
+
+__device__ __forceinline__ int tile_by_work_rank(const int32_t* __restrict__ cu, int ndocs, int R, int n_tiles,
+                                                 int b) {
+  const int lane = threadIdx.x & 63;
+  const bool has_doc = lane < ndocs;
+  return tile_by_work_rank_spans(has_doc, has_doc ? cu[lane] : 0, has_doc ? cu[lane + 1] : 0, R, n_tiles, b);
+}
+
+// The same order for key blocks of R keys under the causal mask, whose work
+// grows with their distance from the end of the document holding their last
+// key: rank the blocks of the mirrored sequence (token p -> n_tiles*R - 1 - p,
+// where the R-aligned padding past N becomes a leading empty document) and
+// map back. Requires ndocs + 1 <= 64.
+__device__ __forceinline__ int key_block_by_work_rank(const int32_t* __restrict__ cu, int ndocs, int N, int R,
+                                                      int n_tiles, int b) {
+  const int lane = threadIdx.x & 63;
+  const int npad = n_tiles * R;
+  // mirrored document l: l = 0 the padding [0, npad - N), l >= 1 the original
+  // document ndocs - l
+  const bool has_doc = lane <= ndocs;
+  int c0 = 0, c1 = 0;
+  if (has_doc) {
+    c0 = lane == 0 ? 0 : npad - cu[ndocs - lane + 1];
+    c1 = lane == 0 ? npad - N : npad - cu[ndocs - lane];
+  }
+  return n_tiles - 1 - tile_by_work_rank_spans(has_doc, c0, c1, R, n_tiles, b);
 }
 
 // Element traits: bf16 uses v_mfma_f32_32x32x16_bf16 (8 k-values per lane),
