@@ -531,10 +531,10 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------
 // bf16 kernels on row-major LDS tiles (lds_tile.hpp): every tile is copied by
-// buffer_load ... lds into a four-stage ring (three tiles ahead), and the transposed operands
-// (Q^T, dO^T, K^T) are read with ds_read_b64_tr_b16 instead of being stored
-// twice. One barrier per tile; a stage is refilled only after the tile's LDS
-// reads (the compiler waits for in-flight LDS copies before transposed reads).
+// buffer_load ... lds (inline assembly, counted by explicit vmcnt waits) into
+// a four-stage ring, three tiles ahead, and the transposed operands (Q^T,
+// dO^T, K^T) are read with ds_read_b64_tr_b16 instead of being stored twice.
+// One barrier per tile; a stage is refilled only after the tile's LDS reads.
 // ----------------------------------------------------------------------------
 template <int D>
 struct DqBf {
@@ -601,9 +601,13 @@ void dq_bf16_kernel(BwdParams p) {
     const int kv0 = t * BT;
     const uint32_t bytes = uint32_t(min(BT, p.N - kv0)) * kv_row;
     const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
-    issue_tile<D, C::kThreads>(make_rsrc(p.k + off, bytes), kv_row, st, tid);
-    issue_tile<D, C::kThreads>(make_rsrc(p.v + off, bytes), kv_row, st + C::TB, tid);
+    issue_tile<D, C::kThreads, 64, true>(make_rsrc_uniform(p.k + off, bytes), kv_row, st, tid);
+    issue_tile<D, C::kThreads, 64, true>(make_rsrc_uniform(p.v + off, bytes), kv_row, st + C::TB, tid);
   };
+  // The tile copies are inline assembly, unknown to the compiler: its own
+  // loads (Q, dO, lse, delta rows) are complete here, so it adds no wait of
+  // its own later that would also drain the copies in flight.
+  wait_vmcnt<0>();
   issue(t0);
   if (t0 + 1 <= t1) issue(t0 + 1);
   if (t0 + 2 <= t1) issue(t0 + 2);

@@ -519,6 +519,10 @@ void attn_fwd_bf16_kernel(FwdParams p, ShardSrc sh) {
   // One loop per group (the barrier counts match), so that each keeps only
   // its own values in registers.
   f32x16_t s[2];
+  // The compiler's own loads (Q rows, document offsets) are complete before
+  // the first copy, so it adds no wait of its own later (at the first masked
+  // tile) that would also drain the copies in flight, which it cannot see.
+  wait_vmcnt<0>();
   for (int i = 0; i < 3; ++i)
     if (t0 + i <= t1) issue(t0 + i, grp_b);
   if (!grp_b) {
