@@ -17,6 +17,7 @@
  *   attn_fwd_from_shards  the same, reading sequence-sharded Q/K/V in place
  *   attn_merge       combine attention results over disjoint key chunks (LSE merge)
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
+ *   attn_bwd_ex      the same with float32 gradients from bf16 inputs
  *   attn_bwd_accumulate  the same, adding to the gradients (chunked attention)
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
  *   ulysses_pack_heads / ulysses_unpack_heads
@@ -285,8 +286,13 @@ uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype d
                                    size_t* bytes);
 
 /*
- * attn_bwd -- gradients of L = sum(dout * o) for attn_fwd's outputs, with the
- * softmax probabilities recomputed from lse:
+ * attn_bwd -- the backward of attn_fwd for one head group. The pages train
+ * with this path ("Ulysses Sequence Parallelism: Training with Million-Token
+ * Contexts", opening paragraph; "Snowflake's Ulysses trick ...", fourth
+ * paragraph: fine-tuning through the same attention handler), so each GPU
+ * also computes the gradients of the attention over its heads (second
+ * paragraph of the same page: heads are independent). With the softmax
+ * probabilities recomputed from lse, the gradients of L = sum(dout * o) are
  *   delta_i = dout_i . o_i
  *   P_ij  = exp(S_ij - lse_i)            dP_ij = dout_i . v_j
  *   dS_ij = P_ij (dP_ij - delta_i)
@@ -295,21 +301,34 @@ uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype d
  *   dv_j  = sum_{h in group} sum_i P_ij dout_i
  * q, o, dout : device [N][hq][D] of dt; k, v : device [N][hk][D] of dt;
  * lse : device float32 [hq][N] from attn_fwd with the same inputs.
- * dq : device [N][hq][D], dk, dv : device [N][hk][D], all of grad_dt, which
- * is dt or ULY_F32 (fp32 gradients from bf16 inputs: the same computation,
- * stored before the final rounding; with grad_dt == dt == ULY_BF16 each
- * gradient is that fp32 value rounded to nearest even).
- * dq, dk, dv are overwritten (dk/dv hold the sum over the G q heads of each
- * kv head). workspace: device memory of at least attn_bwd_workspace_size()
- * bytes, 16-byte aligned, owned by the caller, contents ignored.
+ * dq : device [N][hq][D], dk, dv : device [N][hk][D], all of dt (bf16
+ * gradients are the float32 results rounded to nearest even). They are
+ * overwritten; dk/dv hold the sum over the G q heads of each kv head.
+ * workspace: device memory of at least attn_bwd_workspace_size() bytes,
+ * 16-byte aligned, owned by the caller, contents ignored on entry.
  * causal must match the attn_fwd call that produced o and lse. Other
- * preconditions as attn_fwd. Results are deterministic (no atomics).
+ * preconditions and errors as attn_fwd. Results are bitwise repeatable (no
+ * atomic adds: every sum has a fixed order).
  */
 uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                    int64_t N, int hq, int hk, int D, uly_dtype dt, uly_dtype grad_dt,
+                    int64_t N, int hq, int hk, int D, uly_dtype dt,
                     const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_bwd_ex -- attn_bwd with the gradient type appended to its argument
+ * list: grad_dt is dt, or ULY_F32 for float32 gradients from bf16 inputs
+ * (the same computation, stored before the final rounding). Everything else
+ * as attn_bwd (same workspace size). Errors: ULY_ERR_INVALID_ARG for an
+ * unknown grad_dt, ULY_ERR_UNSUPPORTED for grad_dt other than dt or ULY_F32.
+ */
+uly_status attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       int64_t N, int hq, int hk, int D, uly_dtype dt,
+                       const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       uly_dtype grad_dt);
 
 /*
  * attn_bwd_accumulate -- attn_bwd that adds its gradients to dq, dk and dv
@@ -319,13 +338,13 @@ uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * chunks (attn_merge), one call per (query chunk, key chunk) pair adds that
  * pair's share to the query chunk's dq and the key chunk's dk and dv, and
  * the sums equal the gradients of attention over the union.
- * Same arguments and preconditions as attn_bwd, except that grad_dt must be
- * ULY_F32 (accumulating in bf16 would round at every call; otherwise
- * ULY_ERR_UNSUPPORTED) and dq, dk, dv must hold the values to add to.
+ * Same arguments and preconditions as attn_bwd, except that dq, dk and dv
+ * are float32 whatever dt is (accumulating in bf16 would round at every
+ * call) and must hold the values to add to.
  */
 uly_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o,
                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                               int64_t N, int hq, int hk, int D, uly_dtype dt, uly_dtype grad_dt,
+                               int64_t N, int hq, int hk, int D, uly_dtype dt,
                                const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 

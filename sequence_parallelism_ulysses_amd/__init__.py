@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     ULY_OK,
     UlyssesError,
     attn_bwd,
+    attn_bwd_ex,
     attn_bwd_accumulate,
     attn_bwd_workspace_size,
     attn_fwd,

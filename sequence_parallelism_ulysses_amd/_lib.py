@@ -41,10 +41,12 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _i32, _vp]),
     "attn_merge": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "attn_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
-    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
-                        _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
-    "attn_bwd_accumulate": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
-                                   _vp, _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
+                        _f32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
+                           _f32, _i32, _vp, ctypes.c_size_t, _vp, _i32]),
+    "attn_bwd_accumulate": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
+                                   _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
     "uly_last_error": (ctypes.c_char_p, []),
     "uly_check_cu_seqlens": (_i32, [ctypes.POINTER(ctypes.c_int32), _i32, _i64]),
 }
@@ -312,34 +314,43 @@ def attn_bwd_workspace_size(N: int, hq: int, hk: int, D: int, dtype) -> int:
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, cu_seqlens=None,
              causal: int = 1, stream=None) -> None:
-    """Gradients dq, dk, dv of sum(dout * o) (see include/ulysses.h). The
-    gradient type (grad_dt) is taken from dq: the input type, or float32."""
-    _bwd("attn_bwd", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream)
+    """Gradients dq, dk, dv (of q's dtype) of sum(dout * o) (see include/ulysses.h)."""
+    _bwd("attn_bwd", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream,
+         grad_dtype=q.dtype)
+
+
+def attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, cu_seqlens=None,
+                causal: int = 1, stream=None) -> None:
+    """attn_bwd with the gradient type taken from dq: q's dtype, or float32
+    (see include/ulysses.h)."""
+    _bwd("attn_bwd_ex", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream,
+         grad_dtype=dq.dtype, extra=(_dtype_code(dq),))
 
 
 def attn_bwd_accumulate(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, cu_seqlens=None,
                         causal: int = 1, stream=None) -> None:
     """attn_bwd adding to float32 dq, dk, dv (see include/ulysses.h)."""
+    import torch
     _bwd("attn_bwd_accumulate", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal,
-         stream)
+         stream, grad_dtype=torch.float32)
 
 
-def _bwd(fn, q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream):
+def _bwd(fn, q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream, grad_dtype,
+         extra=()):
     import torch
     N, hq, D = q.shape
     hk = k.shape[1]
     dt = q.dtype
-    gdt = dq.dtype
     args = [_dev(q, (N, hq, D), dt, "q"), _dev(k, (N, hk, D), dt, "k"), _dev(v, (N, hk, D), dt, "v"),
             _dev(o, (N, hq, D), dt, "o"), _dev(dout, (N, hq, D), dt, "dout"),
-            _dev(lse, (hq, N), torch.float32, "lse"), _dev(dq, (N, hq, D), gdt, "dq"),
-            _dev(dk, (N, hk, D), gdt, "dk"), _dev(dv, (N, hk, D), gdt, "dv")]
+            _dev(lse, (hq, N), torch.float32, "lse"), _dev(dq, (N, hq, D), grad_dtype, "dq"),
+            _dev(dk, (N, hk, D), grad_dtype, "dk"), _dev(dv, (N, hk, D), grad_dtype, "dv")]
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     cu, nd = _cu(cu_seqlens, N)
-    _raise(getattr(lib(), fn)(*args, N, hq, hk, D, _dtype_code(q), _dtype_code(dq), cu, nd, float(softmax_scale),
-                              int(causal), ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream)))
+    _raise(getattr(lib(), fn)(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
+                              ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream), *extra))
 
 
 def uly_check_cu_seqlens(host_cu, N: int) -> None:

@@ -402,16 +402,14 @@ namespace {
 
 uly_status bwd_common(const char* fn, int accumulate, const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk,
-                      int D, uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs,
-                      float softmax_scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      int D, uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, uly_dtype grad_dt) {
   uly::AttnDesc d;
   uly_status s = check_attn(fn, N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
   if (s != ULY_OK) return s;
   CHECK(valid_dtype(grad_dt), ULY_ERR_INVALID_ARG, "%s: unknown grad_dt %d", fn, (int)grad_dt);
   CHECK(grad_dt == dt || grad_dt == ULY_F32, ULY_ERR_UNSUPPORTED,
         "%s: grad_dt must equal dt or be ULY_F32", fn);
-  CHECK(!accumulate || grad_dt == ULY_F32, ULY_ERR_UNSUPPORTED,
-        "%s: accumulating gradients requires grad_dt ULY_F32", fn);
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 9; ++i)
@@ -432,19 +430,26 @@ extern "C" {
 
 uly_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
-                    uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale,
-                    int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_common("attn_bwd", 0, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, grad_dt, cu_seqlens, ndocs,
-                    softmax_scale, causal, workspace, workspace_bytes, stream);
+                    uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common("attn_bwd", 0, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, cu_seqlens, ndocs,
+                    softmax_scale, causal, workspace, workspace_bytes, stream, dt);
+}
+
+uly_status attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
+                       uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream, uly_dtype grad_dt) {
+  return bwd_common("attn_bwd_ex", 0, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, cu_seqlens, ndocs,
+                    softmax_scale, causal, workspace, workspace_bytes, stream, grad_dt);
 }
 
 uly_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
-                               uly_dtype dt, uly_dtype grad_dt, const int32_t* cu_seqlens, int ndocs,
-                               float softmax_scale, int causal, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
-  return bwd_common("attn_bwd_accumulate", 1, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, grad_dt,
-                    cu_seqlens, ndocs, softmax_scale, causal, workspace, workspace_bytes, stream);
+                               uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common("attn_bwd_accumulate", 1, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, cu_seqlens,
+                    ndocs, softmax_scale, causal, workspace, workspace_bytes, stream, ULY_F32);
 }
 
 }  // extern "C"

@@ -563,7 +563,7 @@ void dq_bf16_kernel(BwdParams p) {
   // heaviest first: by position in the sequence, or with a few packed
   // documents by position in the document
   const int qtile = (p.cu != nullptr && p.causal && p.ndocs <= 64)
-                        ? uniform(tile_by_work_rank(p.cu, p.ndocs, 32 * QW, p.n_tiles, int(blockIdx.x)))
+                        ? uniform(tile_by_work_rank(p.cu, p.ndocs, p.N, 32 * QW, p.n_tiles, int(blockIdx.x)))
                         : p.n_tiles - 1 - int(blockIdx.x);
   const int wg_q0 = qtile * 32 * QW;
   const int wg_q1 = min(p.N, wg_q0 + 32 * QW);

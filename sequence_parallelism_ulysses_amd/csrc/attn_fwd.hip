@@ -349,7 +349,7 @@ void attn_fwd_bf16_kernel(FwdParams p, ShardSrc sh) {
   // heaviest first: by position in the sequence, or with a few packed
   // documents by position in the document
   const int qtile = (p.cu != nullptr && p.causal && p.ndocs <= 64)
-                        ? uniform(tile_by_work_rank(p.cu, p.ndocs, 32 * QW, p.n_qtiles, int(blockIdx.x)))
+                        ? uniform(tile_by_work_rank(p.cu, p.ndocs, p.N, 32 * QW, p.n_qtiles, int(blockIdx.x)))
                         : p.n_qtiles - 1 - int(blockIdx.x);
   const int wg_q0 = qtile * 32 * QW;
   const int wg_q1 = min(p.N, wg_q0 + 32 * QW);

@@ -66,8 +66,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// An offset of cu_seqlens clamped to [0, N]: malformed offsets (a documented
+// precondition, not checked on the device) then only give wrong results,
+// never index ranges outside the tensors.
+__device__ __forceinline__ int cu_clamped(const int32_t* __restrict__ cu, int i, int N) {
+  return min(max(int(cu[i]), 0), N);
+}
+
 // Document containing token t: offsets cu[0..ndocs] are non-decreasing from
-// 0 to N, and t < N. Returns its [start, end). cu == nullptr: one document.
+// 0 to N, and t < N. Returns its [start, end), both within [0, N].
+// cu == nullptr: one document.
 struct DocSpan {
   int start, end;
 };
@@ -78,7 +86,7 @@ __device__ __forceinline__ DocSpan doc_of(const int32_t* __restrict__ cu, int nd
     const int mid = (lo + hi) >> 1;
     if (cu[mid] <= t) lo = mid; else hi = mid;
   }
-  return {cu[lo], cu[hi]};
+  return {cu_clamped(cu, lo, N), cu_clamped(cu, hi, N)};
 }
 
 // Launch order by causal work with packed documents. Query tile q covers
@@ -127,11 +135,12 @@ __device__ __forceinline__ int tile_by_work_rank_spans(bool has_doc, int c0, int
   return q < 0 ? 0 : (q >= n_tiles ? n_tiles - 1 : q);
 }
 
-__device__ __forceinline__ int tile_by_work_rank(const int32_t* __restrict__ cu, int ndocs, int R, int n_tiles,
-                                                 int b) {
+__device__ __forceinline__ int tile_by_work_rank(const int32_t* __restrict__ cu, int ndocs, int N, int R,
+                                                 int n_tiles, int b) {
   const int lane = threadIdx.x & 63;
   const bool has_doc = lane < ndocs;
-  return tile_by_work_rank_spans(has_doc, has_doc ? cu[lane] : 0, has_doc ? cu[lane + 1] : 0, R, n_tiles, b);
+  return tile_by_work_rank_spans(has_doc, has_doc ? cu_clamped(cu, lane, N) : 0,
+                                 has_doc ? cu_clamped(cu, lane + 1, N) : 0, R, n_tiles, b);
 }
 
 // The same order for key blocks of R keys under the causal mask, whose work
@@ -148,8 +157,8 @@ __device__ __forceinline__ int key_block_by_work_rank(const int32_t* __restrict_
   const bool has_doc = lane <= ndocs;
   int c0 = 0, c1 = 0;
   if (has_doc) {
-    c0 = lane == 0 ? 0 : npad - cu[ndocs - lane + 1];
-    c1 = lane == 0 ? npad - N : npad - cu[ndocs - lane];
+    c0 = lane == 0 ? 0 : npad - cu_clamped(cu, ndocs - lane + 1, N);
+    c1 = lane == 0 ? npad - N : npad - cu_clamped(cu, ndocs - lane, N);
   }
   return n_tiles - 1 - tile_by_work_rank_spans(has_doc, c0, c1, R, n_tiles, b);
 }

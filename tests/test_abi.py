@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_from_shards", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
+        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_from_shards", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
         "ulysses_pack", "ulysses_pack_heads", "ulysses_pack_multi", "ulysses_pack_qkv", "ulysses_unpack",
         "ulysses_unpack_heads", "ulysses_unpack_multi", "ulysses_unpack_qkv"])
 
@@ -260,12 +260,14 @@ def test_attn_fwd_rejects(kw, status, needle):
 
 def _bwd(fn="attn_bwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, N=1024, hq=4, hk=1,
-             D=128, dt=uly.ULY_BF16, gdt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, ws=FAKE, wsb=1 << 30,
-             stream=None)
+             D=128, dt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, ws=FAKE, wsb=1 << 30, stream=None)
+    gdt = kw.pop("gdt", None)
     a.update(kw)
-    return getattr(uly.lib(), fn)(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["N"],
-                              a["hq"], a["hk"], a["D"], a["dt"], a["gdt"], a["cu"], a["nd"], a["scale"], a["causal"], a["ws"],
-                              a["wsb"], a["stream"])
+    args = [a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["N"], a["hq"], a["hk"],
+            a["D"], a["dt"], a["cu"], a["nd"], a["scale"], a["causal"], a["ws"], a["wsb"], a["stream"]]
+    if fn == "attn_bwd_ex":
+        args.append(a["dt"] if gdt is None else gdt)
+    return getattr(uly.lib(), fn)(*args)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -275,21 +277,22 @@ def _bwd(fn="attn_bwd", **kw):
     (dict(ws=None), uly.ULY_ERR_INVALID_ARG, "workspace"),
     (dict(D=256), uly.ULY_ERR_INVALID_ARG, "D=256"),
     (dict(N=-5), uly.ULY_ERR_INVALID_ARG, "N=-5"),
-    (dict(gdt=5), uly.ULY_ERR_INVALID_ARG, "grad_dt"),
-    (dict(dt=uly.ULY_F32, gdt=uly.ULY_BF16), uly.ULY_ERR_UNSUPPORTED, "grad_dt"),
+    (dict(causal=2), uly.ULY_ERR_INVALID_ARG, "causal=2"),
 ])
-def test_attn_bwd_rejects(kw, status, needle):
-    assert _bwd(**kw) == status
+@pytest.mark.parametrize("fn", ["attn_bwd", "attn_bwd_ex", "attn_bwd_accumulate"])
+def test_attn_bwd_rejects(fn, kw, status, needle):
+    assert _bwd(fn, **kw) == status
     assert needle in uly.last_error()
-    acc_kw = dict(gdt=uly.ULY_F32)
-    acc_kw.update(kw)
-    assert _bwd("attn_bwd_accumulate", **acc_kw) == status
-    assert needle in uly.last_error()
+    assert fn in uly.last_error()
 
 
-def test_attn_bwd_accumulate_needs_fp32_gradients():
-    assert _bwd("attn_bwd_accumulate", gdt=uly.ULY_BF16) == uly.ULY_ERR_UNSUPPORTED
-    assert "ULY_F32" in uly.last_error()
+@pytest.mark.parametrize("dt,gdt,status", [
+    (uly.ULY_BF16, 5, uly.ULY_ERR_INVALID_ARG),
+    (uly.ULY_F32, uly.ULY_BF16, uly.ULY_ERR_UNSUPPORTED),
+])
+def test_attn_bwd_ex_rejects_grad_dt(dt, gdt, status):
+    assert _bwd("attn_bwd_ex", dt=dt, gdt=gdt) == status
+    assert "grad_dt" in uly.last_error()
 
 
 def test_workspace_size():
@@ -303,6 +306,9 @@ def test_workspace_size():
 @pytest.mark.parametrize("cu,N,ok", [
     ([0, 5], 5, True), ([0, 3, 3, 5], 5, True), ([0, 0, 5, 5], 5, True),
     ([1, 5], 5, False), ([0, 4, 3, 5], 5, False), ([0, 3], 5, False), ([0], 0, False),
+    # offsets beyond N or negative: rejected on the host (the kernels clamp
+    # them to [0, N] so that such offsets cannot index outside the tensors)
+    ([0, 9, 5], 5, False), ([0, 3, 9], 5, False), ([0, -1, 5], 5, False), ([0, 2, 6, 6], 5, False),
 ])
 def test_check_cu_seqlens(cu, N, ok):
     if ok:
@@ -330,3 +336,97 @@ def test_last_error_is_thread_local():
     th.join()
     assert msgs["t"] == ""
     assert "N=0" in uly.last_error()
+
+
+# ---------------------------------------------------------------------------
+# Prototypes: the header's declarations of the boundary calls, parameter by
+# parameter, and the binding's ctypes signatures derived from them.
+# ---------------------------------------------------------------------------
+def declared_prototypes():
+    """name -> (return type, [(parameter type, parameter name), ...]) from the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?[a-z_]+\s*\*?)\s*([a-z_]+)\s*\(([^;]*?)\)\s*;", text, flags=re.M | re.S):
+        ret, name, params = m.group(1), m.group(2), m.group(3)
+        plist = []
+        for p in params.split(","):
+            p = " ".join(p.split())
+            if p == "void":
+                continue
+            pm = re.match(r"^(.*?[\s*])([A-Za-z_][A-Za-z_0-9]*)$", p)
+            assert pm, (name, p)
+            plist.append((re.sub(r"\s*\*\s*", "* ", pm.group(1)).strip().replace("* *", "**"), pm.group(2)))
+        out[name] = (" ".join(ret.split()), plist)
+    return out
+
+
+# The calls of the boundary as the blueprint of this library states them:
+# argument order, types and names (device pointers, sizes, a stream).
+BOUNDARY = {
+    "ulysses_pack": "const void* const* shards, int P, int64_t T, int H, int D, uly_dtype dt, int group, "
+                    "void* out, hipStream_t stream",
+    "ulysses_unpack": "const void* in, int P, int64_t T, int H, int D, uly_dtype dt, int group, "
+                      "void* const* shards, hipStream_t stream",
+    "attn_fwd": "const void* q, const void* k, const void* v, void* o, float* lse, int64_t N, int hq, int hk, "
+                "int D, uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal, "
+                "hipStream_t stream",
+    "attn_bwd_workspace_size": "int64_t N, int hq, int hk, int D, uly_dtype dt, size_t* bytes",
+    "attn_bwd": "const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, "
+                "void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D, uly_dtype dt, "
+                "const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal, void* workspace, "
+                "size_t workspace_bytes, hipStream_t stream",
+    "uly_last_error": "",
+    "uly_check_cu_seqlens": "const int32_t* host_cu, int ndocs, int64_t N",
+}
+
+
+def _norm_params(text):
+    return [" ".join(p.split()).replace(" *", "*") for p in text.split(",")] if text else []
+
+
+@pytest.mark.parametrize("name", sorted(BOUNDARY))
+def test_boundary_prototype_matches(name):
+    decl = declared_prototypes()[name][1]
+    got = [f"{t} {n}".replace(" *", "*") for t, n in decl]
+    assert got == _norm_params(BOUNDARY[name])
+
+
+def test_extended_backward_calls_extend_the_boundary_list():
+    """attn_bwd_ex is attn_bwd's list plus grad_dt at the end;
+    attn_bwd_accumulate has exactly attn_bwd's list."""
+    protos = declared_prototypes()
+    base = protos["attn_bwd"][1]
+    assert protos["attn_bwd_ex"][1] == base + [("uly_dtype", "grad_dt")]
+    assert protos["attn_bwd_accumulate"][1] == base
+
+
+_SCALAR = {"int": ctypes.c_int, "uly_dtype": ctypes.c_int, "int64_t": ctypes.c_int64, "size_t": ctypes.c_size_t,
+           "float": ctypes.c_float, "uly_status": ctypes.c_int}
+
+
+def _ctypes_ok(ctype, t):
+    t = t.replace("const ", "").strip()
+    if t in _SCALAR:
+        return ctype is _SCALAR[t]
+    if t == "hipStream_t":
+        return ctype is ctypes.c_void_p
+    if t.endswith("**") or t.endswith("* const*") or t.count("*") == 2:
+        return ctype is ctypes.POINTER(ctypes.c_void_p)
+    base = t.rstrip("*").strip()
+    if base in ("void", "float", "char"):
+        return ctype in (ctypes.c_void_p, ctypes.c_char_p)
+    if base in ("int32_t", "int"):
+        return ctype in (ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32))
+    if base == "size_t":
+        return ctype is ctypes.POINTER(ctypes.c_size_t)
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(uly.SIGNATURES))
+def test_binding_signature_follows_the_header(name):
+    ret, params = declared_prototypes()[name]
+    res, args = uly.SIGNATURES[name]
+    assert len(args) == len(params), (name, len(args), len(params))
+    for (t, pname), a in zip(params, args):
+        assert _ctypes_ok(a, t), (name, pname, t, a)
+    assert (res is ctypes.c_char_p) if ret == "const char*" else (res is ctypes.c_int), (name, ret, res)

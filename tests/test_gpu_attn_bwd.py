@@ -37,7 +37,8 @@ def run_fwd_bwd(run, grad_f32=None):
         dq = torch.full(q.shape, float("nan"), dtype=gdt, device=DEV)
         dk = torch.full(k.shape, float("nan"), dtype=gdt, device=DEV)
         dv = torch.full(v.shape, float("nan"), dtype=gdt, device=DEV)
-        uly.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, c.scale, ws, run.cu_dev)
+        bwd = uly.attn_bwd if gdt == q.dtype else uly.attn_bwd_ex
+        bwd(q, k, v, o, do, lse, dq, dk, dv, c.scale, ws, run.cu_dev)
         out.update({"dq" + suffix: dq, "dk" + suffix: dk, "dv" + suffix: dv})
     torch.cuda.synchronize()
     return out

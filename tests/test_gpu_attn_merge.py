@@ -165,7 +165,7 @@ def test_bwd_accumulate_adds_to_the_outputs(N, hq, hk, dtype):
     uly.attn_fwd(q, k, v, o, lse, scale)
     ws = torch.empty(uly.attn_bwd_workspace_size(N, hq, hk, D, tdt), dtype=torch.uint8, device=DEV)
     plain = [torch.empty(t.shape, dtype=torch.float32, device=DEV) for t in (q, k, v)]
-    uly.attn_bwd(q, k, v, o, do, lse, *plain, scale, ws)
+    uly.attn_bwd_ex(q, k, v, o, do, lse, *plain, scale, ws)
     prior = [torch.randn(t.shape, generator=g, device=DEV) for t in (q, k, v)]
     acc = [t.clone() for t in prior]
     uly.attn_bwd_accumulate(q, k, v, o, do, lse, *acc, scale, ws)

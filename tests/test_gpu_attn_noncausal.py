@@ -33,7 +33,8 @@ def run_noncausal(run, backward=True):
         kinds = [("", q.dtype)] + ([("32", torch.float32)] if q.dtype == torch.bfloat16 else [])
         for suffix, gdt in kinds:
             g = {n: torch.full(t.shape, float("nan"), dtype=gdt, device=DEV) for n, t in (("dq", q), ("dk", k), ("dv", v))}
-            uly.attn_bwd(q, k, v, o, do, lse, g["dq"], g["dk"], g["dv"], c.scale, ws, run.cu_dev, causal=0)
+            bwd = uly.attn_bwd if gdt == q.dtype else uly.attn_bwd_ex
+            bwd(q, k, v, o, do, lse, g["dq"], g["dk"], g["dv"], c.scale, ws, run.cu_dev, causal=0)
             out.update({n + suffix: t for n, t in g.items()})
     torch.cuda.synchronize()
     return out

@@ -35,7 +35,7 @@ def _fwd_bwd(q, k, v, do, cu=None, causal=1):
     uly.attn_fwd(q, k, v, o, lse, scale, cu, causal=causal)
     ws = torch.empty(uly.attn_bwd_workspace_size(N, hq, hk, D, q.dtype), dtype=torch.uint8, device=DEV)
     grads = [torch.empty(t.shape, dtype=torch.float32, device=DEV) for t in (q, k, v)]
-    uly.attn_bwd(q, k, v, o, do, lse, *grads, scale, ws, cu, causal=causal)
+    uly.attn_bwd_ex(q, k, v, o, do, lse, *grads, scale, ws, cu, causal=causal)
     torch.cuda.synchronize()
     return o, lse, grads
 
