@@ -32,6 +32,7 @@
 // transposed operand stored a second time); bf16 tiles are copied global ->
 // LDS by buffer loads into row-major, XOR-swizzled rows (lds_tile.hpp) and
 // the transposed operands are read with ds_read_b64_tr_b16.
+#include <algorithm>
 #include <cmath>
 #include <numeric>
 
@@ -56,14 +57,29 @@ constexpr int kKeysPerWg = 32 * kWaves;
 int dkdv_splits(const AttnDesc&) { return 4; }
 
 struct WsLayout {
-  size_t delta, lse2, part, total;
+  size_t delta, lse2, absmax, q16, do16, k16, v16, part, total;
 };
 WsLayout ws_layout(const AttnDesc& d) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WsLayout w;
-  const size_t row_bytes = (size_t(4) * d.hq * d.N + 255) & ~size_t(255);
+  const size_t row_bytes = up(size_t(4) * d.hq * d.N);
   w.delta = 0;
   w.lse2 = row_bytes;
-  w.part = 2 * row_bytes;
+  size_t at = 2 * row_bytes;
+  if (d.dt == ULY_BF16) {
+    // the maxima (kMaxSlots uint32), then the fp16 operand copies
+    w.absmax = at;
+    at += up(kMaxSlots * 4);
+    const size_t qb = up(size_t(2) * d.N * d.hq * d.D), kb = up(size_t(2) * d.N * d.hk * d.D);
+    w.q16 = at;
+    w.do16 = at + qb;
+    w.k16 = at + 2 * qb;
+    w.v16 = at + 2 * qb + kb;
+    at += 2 * qb + 2 * kb;
+  } else {
+    w.absmax = w.q16 = w.do16 = w.k16 = w.v16 = 0;
+  }
+  w.part = at;
   const int s = dkdv_splits(d);
   const size_t part_bytes = s > 1 ? size_t(2) * s * d.N * d.hk * d.D * 4 : 0;
   w.total = w.part + part_bytes;
@@ -105,6 +121,123 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdParams p) {
     p.delta[h * p.N + q] = acc;
     p.lse2[h * p.N + q] = p.lse[h * p.N + q] * kLog2e;
   }
+}
+
+// bf16 inputs: the same delta and lse * log2(e) - 15 (the backward's P
+// carries 2^15), plus what the fp16 operand scales derive from (BwdScales):
+// the largest |value| of q, k, v and dout and the largest row norms of dout
+// and v. A grid-stride loop over rows, so that each workgroup ends with one
+// atomic max per quantity.
+__device__ __forceinline__ uint32_t absmax_bf16x8(u32x4_t x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = max(m, max(x[j] & 0x7fffu, (x[j] >> 16) & 0x7fffu));
+  return m;
+}
+__device__ __forceinline__ float sumsq_bf16x8(u32x4_t x) {
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = bf16_bits_to_f32(x[j] & 0xffffu), hi = bf16_bits_to_f32(x[j] >> 16);
+    a = fmaf(lo, lo, fmaf(hi, hi, a));
+  }
+  return a;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prep_bf16_kernel(BwdParams p) {
+  constexpr int LPR = D * 2 / 16;       // lanes per row (16 bytes each)
+  constexpr int RPB = kThreads / LPR;   // rows per workgroup and step
+  const int sub = threadIdx.x % LPR;
+  const int64_t rows_q = int64_t(p.N) * p.hq, rows_k = int64_t(p.N) * p.hk;
+  // maxima as bit patterns of non-negative values (ordered like the values)
+  uint32_t m[6] = {0, 0, 0, 0, 0, 0};  // q, k, v, dout (bf16 bits), |dout row|^2, |v row|^2 (fp32 bits)
+  for (int64_t row0 = int64_t(blockIdx.x) * RPB; row0 < rows_q; row0 += int64_t(gridDim.x) * RPB) {
+    const int64_t row = row0 + threadIdx.x / LPR;
+    float acc = 0.f, nd = 0.f, nv = 0.f;
+    if (row < rows_q) {
+      const int64_t off = row * D * 2 + sub * 16;  // row = token * hq + head (or token * hk + head)
+      const u32x4_t x = ld16(p.o + off), y = ld16(p.dout + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(bf16_bits_to_f32(x[j] & 0xffffu), bf16_bits_to_f32(y[j] & 0xffffu), acc);
+        acc = fmaf(bf16_bits_to_f32(x[j] >> 16), bf16_bits_to_f32(y[j] >> 16), acc);
+      }
+      m[3] = max(m[3], absmax_bf16x8(y));
+      nd = sumsq_bf16x8(y);
+      m[0] = max(m[0], absmax_bf16x8(ld16(p.q + off)));
+      if (row < rows_k) {
+        const u32x4_t vv = ld16(p.v + off);
+        m[1] = max(m[1], absmax_bf16x8(ld16(p.k + off)));
+        m[2] = max(m[2], absmax_bf16x8(vv));
+        nv = sumsq_bf16x8(vv);
+      }
+    }
+#pragma unroll
+    for (int s = LPR / 2; s >= 1; s >>= 1) {
+      acc += __shfl_xor(acc, s, LPR);
+      nd += __shfl_xor(nd, s, LPR);
+      nv += __shfl_xor(nv, s, LPR);
+    }
+    m[4] = max(m[4], __float_as_uint(nd));
+    m[5] = max(m[5], __float_as_uint(nv));
+    if (row < rows_q && sub == 0) {
+      const int64_t q = row / p.hq, h = row % p.hq;
+      p.delta[h * p.N + q] = acc;
+      p.lse2[h * p.N + q] = p.lse[h * p.N + q] * kLog2e - 15.f;
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1)
+#pragma unroll
+    for (int i = 0; i < 6; ++i) m[i] = max(m[i], uint32_t(__shfl_xor(int(m[i]), s)));
+  __shared__ uint32_t wmax[kWaves][6];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int i = 0; i < 6; ++i) wmax[w][i] = m[i];
+  __syncthreads();
+  if (threadIdx.x < 6) {
+    uint32_t x = 0;
+    for (int i = 0; i < kWaves; ++i) x = max(x, wmax[i][threadIdx.x]);
+    atomicMax(p.absmax + 64 * threadIdx.x, x);
+  }
+}
+
+// Zero the maxima before prep_bf16_kernel (a kernel rather than a memset,
+// so that the call can be captured in a graph).
+__global__ void absmax_init_kernel(uint32_t* absmax) {
+  if (threadIdx.x < kMaxSlots / 64) absmax[64 * threadIdx.x] = 0u;
+}
+
+// fp16 copies of q, dout, k and v, each scaled by its power of two
+// (BwdScales), and delta rescaled to delta * 2^(eds-15). Every conversion is
+// exact except the rounding of values below 2^-21 of a tensor's largest.
+template <int D>
+__global__ __launch_bounds__(kThreads) void convert_bf16_kernel(BwdParams p) {
+  const float fq = ldexpf(1.f, fp16_scale_exp(p.absmax[kMaxQ])), fk = ldexpf(1.f, fp16_scale_exp(p.absmax[kMaxK]));
+  const float fv = ldexpf(1.f, fp16_scale_exp(p.absmax[kMaxV])), fdo = ldexpf(1.f, fp16_scale_exp(p.absmax[kMaxDo]));
+  const float fdl = ldexpf(1.f, ds_scale_exp(p.absmax[kNormDo], p.absmax[kNormV]) - 15);
+  const int64_t nq = int64_t(p.N) * p.hq * D / 8, nk = int64_t(p.N) * p.hk * D / 8;  // 16-byte chunks
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < 2 * (nq + nk); i += stride) {
+    const char* src;
+    char* dst;
+    float f;
+    int64_t j = i;
+    if (j < nq) { src = p.q; dst = p.q16; f = fq; }
+    else if ((j -= nq) < nq) { src = p.dout; dst = p.do16; f = fdo; }
+    else if ((j -= nq) < nk) { src = p.k; dst = p.k16; f = fk; }
+    else { j -= nk; src = p.v; dst = p.v16; f = fv; }
+    const u32x4_t x = ld16(src + 16 * j);
+    u32x4_t y;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      y[w] = pack_f16x2(bf16_bits_to_f32(x[w] & 0xffffu) * f, bf16_bits_to_f32(x[w] >> 16) * f);
+    *reinterpret_cast<u32x4_t*>(dst + 16 * j) = y;
+  }
+  const int64_t nd = int64_t(p.N) * p.hq;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nd; i += stride) p.delta[i] *= fdl;
 }
 
 // ----------------------------------------------------------------------------
@@ -340,6 +473,13 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int 
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= n4) return;
   const int64_t stride = int64_t(p.N) * p.hk * D;
+  // bf16 inputs: undo the fp16 operand scales (BwdScales); fp32: dK's scale
+  float mul_k = p.scale, mul_v = 1.f;
+  if (p.absmax != nullptr) {
+    const BwdScales sc = bwd_scales(p.absmax, p.scale);
+    mul_k = sc.mul_dk;
+    mul_v = sc.mul_dv;
+  }
   float k[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < p.splits; ++s) {
     const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.part_dk + s * stride + 4 * i);
@@ -351,7 +491,10 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int 
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) k[j] *= p.scale;
+  for (int j = 0; j < 4; ++j) {
+    k[j] *= mul_k;
+    v[j] *= mul_v;
+  }
   constexpr int OE = kF32Out ? 4 : 2;
   store4<kF32Out>(p.dk + 4 * i * OE, k, p.accumulate);
   store4<kF32Out>(p.dv + 4 * i * OE, v, p.accumulate);
@@ -575,6 +718,7 @@ void dq_bf16_kernel(BwdParams p) {
   const bool q_ok = my_q < p.N;
   const QueryBounds qbd(p, my_q, qbase, wq_last, active);
   const int my_ds = qbd.my_ds, my_hi = qbd.my_hi;
+  const BwdScales sc = bwd_scales(p.absmax, p.scale);
   const float my_lse2 = q_ok ? p.lse2[int64_t(head) * p.N + my_q] : 0.f;
   const float my_dlt = q_ok ? p.delta[int64_t(head) * p.N + my_q] : 0.f;
 
@@ -583,8 +727,8 @@ void dq_bf16_kernel(BwdParams p) {
     const int64_t off = (int64_t(my_q) * p.hq + head) * D * 2 + half * 16;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      qf[ks] = q_ok ? *reinterpret_cast<const bf16x8_t*>(p.q + off + ks * 32) : bf16x8_t{};
-      df[ks] = q_ok ? *reinterpret_cast<const bf16x8_t*>(p.dout + off + ks * 32) : bf16x8_t{};
+      qf[ks] = q_ok ? *reinterpret_cast<const bf16x8_t*>(p.q16 + off + ks * 32) : bf16x8_t{};
+      df[ks] = q_ok ? *reinterpret_cast<const bf16x8_t*>(p.do16 + off + ks * 32) : bf16x8_t{};
     }
   }
   f32x16_t dqt[C::DB];
@@ -601,8 +745,8 @@ void dq_bf16_kernel(BwdParams p) {
     const int kv0 = t * BT;
     const uint32_t bytes = uint32_t(min(BT, p.N - kv0)) * kv_row;
     const int64_t off = (int64_t(kv0) * p.hk + kvh) * D * 2;
-    issue_tile<D, C::kThreads, 64, true>(make_rsrc_uniform(p.k + off, bytes), kv_row, st, tid);
-    issue_tile<D, C::kThreads, 64, true>(make_rsrc_uniform(p.v + off, bytes), kv_row, st + C::TB, tid);
+    issue_tile<D, C::kThreads, 64, true>(make_rsrc_uniform(p.k16 + off, bytes), kv_row, st, tid);
+    issue_tile<D, C::kThreads, 64, true>(make_rsrc_uniform(p.v16 + off, bytes), kv_row, st + C::TB, tid);
   };
   // The tile copies are inline assembly, unknown to the compiler: its own
   // loads (Q, dO, lse, delta rows) are complete here, so it adds no wait of
@@ -626,8 +770,8 @@ void dq_bf16_kernel(BwdParams p) {
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = mfma(frag_rows<D>(kr, kb * 32 + l32, ks * 16, half), qf[ks], s[kb]);
-          dp[kb] = mfma(frag_rows<D>(vr, kb * 32 + l32, ks * 16, half), df[ks], dp[kb]);
+          s[kb] = mfma_f16(frag_rows<D>(kr, kb * 32 + l32, ks * 16, half), qf[ks], s[kb]);
+          dp[kb] = mfma_f16(frag_rows<D>(vr, kb * 32 + l32, ks * 16, half), df[ks], dp[kb]);
         }
       // masked scores become -inf (their exponentials exact zeros) in a loop
       // of their own, so the exponentials below are one straight run
@@ -645,15 +789,17 @@ void dq_bf16_kernel(BwdParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[kb][r], p.scale_log2, -my_lse2));
-          dsv[kb * 16 + r] = e * (dp[kb][r] - my_dlt);
+          // e = P * 2^15, dsv = dS * 2^eds (see BwdScales)
+          const float e = fast_exp2(fmaf(s[kb][r], sc.c_s, -my_lse2));
+          dsv[kb * 16 + r] = e * fmaf(dp[kb][r], sc.kd, -my_dlt);
         }
       // dQ^T += K^T dS^T, K^T read transposed from the row-major K tile
 #pragma unroll
       for (int st2 = 0; st2 < BT / 16; ++st2) {
-        const bf16x8_t sf = make_frag<TrBF16>(&dsv[st2 * 8]);
+        const bf16x8_t sf = make_frag_f16(&dsv[st2 * 8]);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) dqt[db] = mfma(frag_cols_tr<D>(kr, st2 * 16, db * 32, lane), sf, dqt[db]);
+        for (int db = 0; db < C::DB; ++db)
+          dqt[db] = mfma_f16(frag_cols_tr<D>(kr, st2 * 16, db * 32, lane), sf, dqt[db]);
       }
     }
     if (t + 3 <= t1) issue(t + 3);
@@ -669,7 +815,7 @@ void dq_bf16_kernel(BwdParams p) {
         const int d = db * 32 + 8 * r4 + 4 * half;
         float x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = dqt[db][4 * r4 + j] * p.scale;
+        for (int j = 0; j < 4; ++j) x[j] = dqt[db][4 * r4 + j] * sc.mul_dq;
         store4<kF32Out>(dst + d * OE, x, p.accumulate);
       }
   }
@@ -692,6 +838,13 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   p.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.delta);
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse2);
   p.splits = dkdv_splits(d);
+  char* ws = static_cast<char*>(workspace);
+  const bool half_ops = Tr::kElem == 2;  // bf16 inputs: fp16 operand copies (BwdScales)
+  p.absmax = half_ops ? reinterpret_cast<uint32_t*>(ws + wl.absmax) : nullptr;
+  p.q16 = half_ops ? ws + wl.q16 : nullptr;
+  p.do16 = half_ops ? ws + wl.do16 : nullptr;
+  p.k16 = half_ops ? ws + wl.k16 : nullptr;
+  p.v16 = half_ops ? ws + wl.v16 : nullptr;
   p.part_dk = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part);
   p.part_dv = p.part_dk + (p.splits > 1 ? size_t(p.splits) * d.N * d.hk * d.D : 0);
   p.cu = d.cu;
@@ -708,9 +861,19 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
 
   const int64_t rows = d.N * d.hq;
   const int64_t rows_per_block = kThreads / (D * Tr::kElem / 16);
-  delta_kernel<Tr, D><<<dim3(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block)), kThreads, 0,
-                        stream>>>(p);
-  hipError_t e = hipGetLastError();
+  const int64_t row_blocks = (rows + rows_per_block - 1) / rows_per_block;
+  hipError_t e;
+  if constexpr (Tr::kElem == 2) {
+    // delta, lse2 and the maxima, then the scaled fp16 copies; a few
+    // thousand workgroups loop over the rows (one atomic max per workgroup)
+    const unsigned prep_blocks = static_cast<unsigned>(std::min<int64_t>(row_blocks, 4096));
+    absmax_init_kernel<<<1, 64, 0, stream>>>(p.absmax);
+    prep_bf16_kernel<D><<<dim3(prep_blocks), kThreads, 0, stream>>>(p);
+    convert_bf16_kernel<D><<<dim3(4096), kThreads, 0, stream>>>(p);
+  } else {
+    delta_kernel<Tr, D><<<dim3(static_cast<unsigned>(row_blocks)), kThreads, 0, stream>>>(p);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   p.n_tiles = static_cast<int>((d.N + kKeysPerWg - 1) / kKeysPerWg);

@@ -74,6 +74,7 @@ void dkdv_bf16_kernel(BwdParams p) {
   const int my_lo = kbd.my_lo, my_de = kbd.my_de;
   const int w_de_first = kbd.w_de_first, w_de_last = kbd.w_de_last;
   const uint32_t q_row = uint32_t(p.hq) * D * 2;
+  const BwdScales sc = bwd_scales(p.absmax, p.scale);
 
   // Queries that can see any of the 128 keys: [first_query(kv0), end of
   // the last key's document). The (query tile, q head) iterations over them, tiles from the
@@ -113,8 +114,8 @@ void dkdv_bf16_kernel(BwdParams p) {
       const int64_t off = (int64_t(key) * p.hk + kvh) * D * 2 + half * 16;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        kf[ks] = key < p.N ? *reinterpret_cast<const bf16x8_t*>(p.k + off + ks * 32) : bf16x8_t{};
-        vf[ks] = key < p.N ? *reinterpret_cast<const bf16x8_t*>(p.v + off + ks * 32) : bf16x8_t{};
+        kf[ks] = key < p.N ? *reinterpret_cast<const bf16x8_t*>(p.k16 + off + ks * 32) : bf16x8_t{};
+        vf[ks] = key < p.N ? *reinterpret_cast<const bf16x8_t*>(p.v16 + off + ks * 32) : bf16x8_t{};
       }
     }
     RowFragOffsets<D> ro;  // rows l%32 of a tile, k = 16 ks + 8 half
@@ -149,8 +150,8 @@ void dkdv_bf16_kernel(BwdParams p) {
         f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          s = mfma(qa[ks], kf[ks], s);
-          dp = mfma(da[ks], vf[ks], dp);
+          s = mfma_f16(qa[ks], kf[ks], s);
+          dp = mfma_f16(da[ks], vf[ks], dp);
         }
         auto probs = [&](auto masked) {
           float pv[16], dsv[16];
@@ -160,19 +161,20 @@ void dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int r = 4 * r4 + j;
-              float e = fast_exp2(fmaf(s[r], p.scale_log2, -l4[r4][j]));
+              // e = P * 2^15, dsv = dS * 2^eds (see BwdScales)
+              float e = fast_exp2(fmaf(s[r], sc.c_s, -l4[r4][j]));
               if constexpr (decltype(masked)::value) {
                 const int q = qs + qi + j;
                 if (q < my_lo || q >= my_de) e = 0.f;
               }
               pv[r] = e;
-              dsv[r] = e * (dp[r] - d4[r4][j]);
+              dsv[r] = e * fmaf(dp[r], sc.kd, -d4[r4][j]);
             }
           }
 #pragma unroll
           for (int st2 = 0; st2 < 2; ++st2) {
-            *(lds_frag*)pds_at(it, kb, st2) = make_frag<TrBF16>(&pv[st2 * 8]);
-            *(lds_frag*)pds_at(it, kb, 2 + st2) = make_frag<TrBF16>(&dsv[st2 * 8]);
+            *(lds_frag*)pds_at(it, kb, st2) = make_frag_f16(&pv[st2 * 8]);
+            *(lds_frag*)pds_at(it, kb, 2 + st2) = make_frag_f16(&dsv[st2 * 8]);
           }
         };
         // the element-wise mask only on tiles before some key's first query (the
@@ -213,8 +215,8 @@ void dkdv_bf16_kernel(BwdParams p) {
     const int qs = tile_q0(it);
     const int rows = min(C::QT, p.N - qs);
     const int64_t off = (int64_t(qs) * p.hq + head) * D * 2;
-    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.q + off, uint32_t(rows) * q_row), q_row, st, ctid);
-    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.dout + off, uint32_t(rows) * q_row), q_row,
+    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.q16 + off, uint32_t(rows) * q_row), q_row, st, ctid);
+    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.do16 + off, uint32_t(rows) * q_row), q_row,
                                             st + C::TQ, ctid);
     // lse2 and delta of the tile's rows (every consumer wave copies the same values)
     const int64_t foff = int64_t(head) * p.N + qs;
@@ -242,8 +244,8 @@ void dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           const bf16x8_t a = frag_tr_at(src, to.off[0][db] + k0, to.off[1][db] + k0);
-          acc[0][db] = mfma(a, f0, acc[0][db]);
-          acc[1][db] = mfma(a, f1, acc[1][db]);
+          acc[0][db] = mfma_f16(a, f0, acc[0][db]);
+          acc[1][db] = mfma_f16(a, f1, acc[1][db]);
         }
       }
     }
@@ -269,7 +271,7 @@ void dkdv_bf16_kernel(BwdParams p) {
     } else {
       constexpr int OE = kF32Out ? 4 : 2;
       char* out = dk_role ? p.dk : p.dv;
-      const float mul = dk_role ? p.scale : 1.f;
+      const float mul = dk_role ? sc.mul_dk : sc.mul_dv;
       const int64_t off = (int64_t(bkey) * p.hk + kvh) * D * OE;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)

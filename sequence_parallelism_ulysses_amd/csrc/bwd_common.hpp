@@ -23,6 +23,14 @@ struct BwdParams {
   float* lse2;     // lse * log2(e), [hq][N]
   float* part_dk;  // [splits][N][hk][D] fp32, when splits > 1
   float* part_dv;
+  // bf16 inputs: fp16 copies of q, dout ([N][hq][D]) and k, v ([N][hk][D]),
+  // each scaled by a power of two, and the largest |value| of each input
+  // tensor (bf16 bits: q, k, v, dout) that the scales derive from
+  char* q16;
+  char* do16;
+  char* k16;
+  char* v16;
+  uint32_t* absmax;
   const int32_t* cu;
   int ndocs;
   int N, hq, hk, G, Gw;
@@ -32,6 +40,72 @@ struct BwdParams {
   int accumulate;  // 1: add the gradients to dq, dk, dv (fp32 outputs only) instead of overwriting
   float scale, scale_log2;
 };
+
+// Power-of-two scales of the fp16 operands of the bf16-input backward.
+// Tensor x (q, k, v, dout) with max |x| < 2^kx is stored as x * 2^sx with
+// sx <= 15 - kx, so its fp16 copy stays below 2^15 (fp16's largest finite
+// value is 65504) and keeps bf16's 8 significant bits exactly down to at
+// least 2^-21 of its largest value. The products then carry 2^(sq+sk) (S) and
+// 2^(sdo+sv) (dP). With P <= 1, |dP_ij| <= |dO_i| |v_j| and |delta_i| <=
+// |dO_i| |O_i| <= |dO_i| max_j |v_j| (row 2-norms; O is a convex combination
+// of the v rows), |dS| <= 2.01 max|dO| max|v| < 2^(ndo+nv+2) for row norms
+// below 2^ndo and 2^nv, so dS is stored as dS * 2^eds with eds <= 13 - ndo -
+// nv, and P as P * 2^15. Each exponent is rounded down to a multiple of 8: for
+// data of ordinary range (unit-scale inputs, or inputs a few times larger)
+// the scales then do not move when some values change, so that results
+// depend on other rows' data only where the mathematics says so. Every scale
+// is exact, and each output is scaled back once in its epilogue.
+struct BwdScales {
+  float c_s;     // scale*log2(e)*2^-(sq+sk): S in exp2 units
+  float kd;      // 2^(eds-15-sdo-sv): dP in the units of delta * 2^(eds-15)
+  float mul_dq;  // scale * 2^-(eds+sk)
+  float mul_dk;  // scale * 2^-(eds+sq)
+  float mul_dv;  // 2^-(15+sdo)
+};
+
+// Slots of the maxima in the workspace (uint32 index, 256 bytes apart):
+// max |x| as bf16 bits for q, k, v, dout, then the largest squared row norm
+// (fp32 bits) of dout and v.
+enum { kMaxQ = 0, kMaxK = 64, kMaxV = 128, kMaxDo = 192, kNormDo = 256, kNormV = 320, kMaxSlots = 384 };
+
+// Exponent bound of a bf16 |value| bit pattern: |x| < 2^k. Zero and
+// subnormals give -126; inf/NaN give 0 (the results are not finite anyway).
+__host__ __device__ __forceinline__ int exp_bound_bf16(uint32_t bits) {
+  const int e = int((bits >> 7) & 0xff);
+  if (e == 0xff) return 0;
+  return e == 0 ? -126 : e - 126;
+}
+// Exponent bound of a norm from its square (fp32 bits): |x| < 2^k.
+__host__ __device__ __forceinline__ int exp_bound_norm2(uint32_t bits) {
+  const int e = int((bits >> 23) & 0xff);
+  if (e == 0xff) return 0;
+  const int e2 = e == 0 ? -126 : e - 126;  // norm^2 < 2^e2
+  return (e2 + 1) >> 1;                     // ceil(e2 / 2)
+}
+// The largest multiple of 8 not above x, within the fp32 exponent range.
+__host__ __device__ __forceinline__ int quant_exp(int x) {
+  const int q = x >= 0 ? x / 8 * 8 : -((-x + 7) / 8 * 8);
+  return q < -120 ? -120 : (q > 120 ? 120 : q);
+}
+__host__ __device__ __forceinline__ int fp16_scale_exp(uint32_t max_bits) {
+  return quant_exp(15 - exp_bound_bf16(max_bits));
+}
+__host__ __device__ __forceinline__ int ds_scale_exp(uint32_t norm2_do_bits, uint32_t norm2_v_bits) {
+  return quant_exp(13 - exp_bound_norm2(norm2_do_bits) - exp_bound_norm2(norm2_v_bits));
+}
+
+__device__ __forceinline__ BwdScales bwd_scales(const uint32_t* absmax, float scale) {
+  const int sq = fp16_scale_exp(absmax[kMaxQ]), sk = fp16_scale_exp(absmax[kMaxK]);
+  const int sv = fp16_scale_exp(absmax[kMaxV]), sdo = fp16_scale_exp(absmax[kMaxDo]);
+  const int eds = ds_scale_exp(absmax[kNormDo], absmax[kNormV]);
+  BwdScales b;
+  b.c_s = ldexpf(scale * kLog2e, -(sq + sk));
+  b.kd = ldexpf(1.f, eds - 15 - sdo - sv);
+  b.mul_dq = ldexpf(scale, -(eds + sk));
+  b.mul_dk = ldexpf(scale, -(eds + sq));
+  b.mul_dv = ldexpf(1.f, -(15 + sdo));
+  return b;
+}
 
 // Visibility bounds of a query-stationary wave (32 rows from qbase, last
 // valid row wq_last): row i sees keys [doc start, hi(i)], hi(i) = i when

@@ -32,6 +32,17 @@ __device__ __forceinline__ f32x16_t mfma(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// fp16 variant of the same product. The backward of bf16 inputs runs its
+// products on fp16 operands (11 significant bits against bf16's 8, same MFMA
+// rate): inputs are copied to fp16 with a power-of-two scale per tensor, and
+// the probabilities and dS are rounded to fp16 instead of bf16. The operands
+// travel in the same 16-bit fragment type the LDS readers return.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16_t mfma_f16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
 // Combine a per-lane value with the same lane of the other half-wave
 // (lane l and lane l^32): v_permlane32_swap hands each lane both values.
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -65,6 +76,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> two fp16 (round to nearest even) in one 32-bit word
+// (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+// Eight fp32 values as an fp16 MFMA fragment (see mfma_f16).
+__device__ __forceinline__ bf16x8_t make_frag_f16(const float* v) {
+  u32x4_t w;
+  w[0] = pack_f16x2(v[0], v[1]);
+  w[1] = pack_f16x2(v[2], v[3]);
+  w[2] = pack_f16x2(v[4], v[5]);
+  w[3] = pack_f16x2(v[6], v[7]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
 
 // An offset of cu_seqlens clamped to [0, N]: malformed offsets (a documented
 // precondition, not checked on the device) then only give wrong results,

@@ -47,6 +47,26 @@ def bf16_tol(ref: np.ndarray, base: float = 2e-2) -> np.ndarray:
     return np.maximum(base, np.exp2(e - 7))
 
 
+def grad_tol(ref: np.ndarray, G: int, name: str) -> np.ndarray:
+    """The bf16 gradient bar: bf16_tol(ref). dK and dV of a kv head sum the
+    gradients of its G query heads, so their rounding errors add up over G
+    independent terms; the 2e-2 bar is stated for the workloads' G = 4, and
+    for larger G the base grows as sqrt(G / 4)."""
+    base = 2e-2 * max(1.0, (G / 4) ** 0.5) if name in ("dk", "dv") else 2e-2
+    return bf16_tol(ref, base)
+
+
+def err_report(what: str, got: np.ndarray, ref: np.ndarray) -> str:
+    """Max-abs error, max |ref|, the count of elements whose error exceeds
+    2e-2, and the worst error relative to bf16_tol; printed and returned."""
+    err = np.abs(got - ref)
+    line = (f"{what}: max err {err.max():.4g}, max |ref| {np.abs(ref).max():.4g}, "
+            f"{int((err > 2e-2).sum())} of {err.size} elements above 2e-2, "
+            f"worst err / max(2e-2, ulp) = {(err / bf16_tol(ref)).max():.3f}")
+    print(line, flush=True)
+    return line
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, tol, what: str):
     err = np.abs(got - ref)
     bad = err > tol

@@ -3,12 +3,14 @@ against the fp64 oracle.
 
 Tolerances:
   - fp32 workload: max-abs <= 1e-4.
-  - bf16 inputs: the gradients are computed once more with fp32 outputs
-    (grad_dt = fp32, the same arithmetic stored before the final rounding);
-    those must be within max-abs 2e-2 of the oracle, and the bf16 gradients
-    must equal their round-to-nearest-even bit for bit. So every bf16
-    gradient is within 2e-2 plus half a bf16 ulp of the exact value; the
-    final rounding alone can cost half an ulp (0.0078 at |x| in [2, 4)).
+  - bf16 inputs: every bf16 gradient element within max(2e-2, one bf16 ulp of
+    |ref|) of the exact value (the bar is 2e-2 wherever 2e-2 is attainable,
+    |ref| < 8; above that a correctly rounded bf16 value can be half an ulp
+    off). dK and dV sum G query heads' gradients; beyond the workloads' G = 4
+    their base grows as sqrt(G/4) (harness.grad_tol). The gradients are also computed with fp32 outputs (attn_bwd_ex,
+    the same arithmetic stored before the final rounding): those must be
+    within max-abs 2e-2, and the bf16 gradients must equal their
+    round-to-nearest-even bit for bit.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,8 @@ import torch
 import sequence_parallelism_ulysses_amd as uly
 import synthetic as syn
 from oracle import attn_ref, unpack_ref
-from harness import (DEV, Run, assert_close, bf16_tol, decode, dev_to_bits, oracle_attention, sample_rows)
+from harness import (DEV, Run, assert_close, bf16_tol, decode, dev_to_bits, err_report, grad_tol,
+                     oracle_attention, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +64,9 @@ def check_grad(cfg, got, ref_vals, name, sel=slice(None), ref_sel=slice(None)):
         return
     g32 = got[name + "32"][sel]
     assert_close(g32.cpu().numpy().astype(np.float64), ref, 2e-2, name + " (fp32 out)")
+    val = decode(dev_to_bits(got[name][sel]))
+    err_report(name, val, ref)
+    assert_close(val, ref, grad_tol(ref, cfg.hq // cfg.hk, name), name)
     assert np.array_equal(dev_to_bits(got[name][sel]), _rne_bits(g32)), name + ": bf16 != RNE(fp32)"
 
 
@@ -89,6 +95,10 @@ SMALL = [
     (64, 1, 4, 1, 64, "f32", [10, 54]),
     (8, 8, 8, 8, 128, "bf16", None),
     (200, 2, 4, 2, 64, "f32", [33, 0, 167]),
+    (1000, 4, 32, 4, 128, "bf16", None),                # G = 8: one 32-row tile per workgroup, 8 heads
+    (1536, 2, 32, 2, 128, "bf16", [700, 836]),          # G = 16: two head groups per kv head
+    (640, 1, 8, 1, 64, "bf16", [100, 1, 539]),          # G = 8, D = 64
+    (512, 2, 64, 4, 128, "bf16", None),                 # G = 16 over two kv heads
 ]
 
 
@@ -147,31 +157,44 @@ def test_bwd_c2_full():
     check_grads(cfg, got, oracle_attention(run))
 
 
-def test_bwd_c3_sampled_rows_and_tail_columns():
-    """128k tokens: dQ on sampled rows; dK/dV exactly on the last 1024 key
-    columns (only rows >= N-1024 reach them); document sum rules overall."""
+def _sum_rules(dk, dv, do):
+    """Document sum rules over every key column of one document: sum_j dK_j = 0
+    (softmax is invariant to shifting every score of a row) and sum_j dV_j =
+    sum over heads and rows of dO. Returns both residues relative to the
+    summed magnitudes."""
+    rk = np.abs(dk.sum(axis=0)) / np.abs(dk).sum(axis=0)
+    rv = np.abs(dv.sum(axis=0) - do.sum(axis=(0, 1))) / np.abs(dv).sum(axis=0)
+    return float(rk.max()), float(rv.max())
+
+
+@pytest.mark.timeout(1200)
+def test_bwd_c3_full():
+    """The Llama-3.1-8B-shaped head group at 128k tokens, every element of O,
+    LSE, dQ, dK and dV against the oracle (computed in eight blocks of query
+    rows, whose dK/dV contributions add up), and the document sum rules."""
     cfg = syn.CONFIGS["c3"]
     run = Run(cfg)
     got = run_fwd_bwd(run)
-    rows = sample_rows(cfg.N, None, n_random=48)
-    tail = cfg.N - 1024
-    ref_rows = oracle_attention(run, rows=rows)
-    check_grad(cfg, got, ref_rows, "dq", sel=torch.from_numpy(rows).to(DEV))
-    ref_tail = oracle_attention(run, rows=np.arange(tail, cfg.N))
-    for name in ("dk", "dv"):
-        check_grad(cfg, got, ref_tail, name, sel=slice(tail, None), ref_sel=slice(tail, None))
-    # sum rules over the whole (single) document, a check of every column at
-    # once: sum_j dK_j = 0 and sum_j dV_j = sum over heads and rows of dO.
-    # Bound: 1% of the summed magnitudes (rounding of bf16 outputs and of the
-    # bf16 P/dS operands leaves a residue far below that; a dropped or doubled
-    # query tile does not).
-    dk = decode(dev_to_bits(got["dk"]))[:, 0]
-    dv = decode(dev_to_bits(got["dv"]))[:, 0]
-    do = decode(dev_to_bits(run.packed("do")))
-    rk = np.abs(dk.sum(axis=0)) / np.abs(dk).sum(axis=0)
-    rv = np.abs(dv.sum(axis=0) - do.sum(axis=(0, 1))) / np.abs(dv).sum(axis=0)
-    print(f"sum rules: max |sum dK|/sum|dK| = {rk.max():.3g}, max |sum dV - sum dO|/sum|dV| = {rv.max():.3g}")
-    assert rk.max() < 1e-2 and rv.max() < 1e-2
+    N = cfg.N
+    ref = {"o": np.zeros((N, cfg.hq, cfg.D)), "lse": np.zeros((cfg.hq, N)), "dq": np.zeros((N, cfg.hq, cfg.D)),
+           "dk": np.zeros((N, cfg.hk, cfg.D)), "dv": np.zeros((N, cfg.hk, cfg.D))}
+    x = run.oracle_inputs()
+    for b in range(8):
+        rows = np.arange(b * N // 8, (b + 1) * N // 8)
+        part = attn_ref(x["q"], x["k"], x["v"], cfg.scale, None, do=x["do"], rows=rows)
+        ref["o"][rows], ref["lse"][:, rows], ref["dq"][rows] = part["o"], part["lse"], part["dq"]
+        ref["dk"] += part["dk"]
+        ref["dv"] += part["dv"]
+        print(f"c3 oracle: rows up to {rows[-1] + 1} of {N}", flush=True)
+    got_o = decode(dev_to_bits(got["o"]))
+    err_report("O", got_o, ref["o"])
+    assert_close(got_o, ref["o"], bf16_tol(ref["o"]), "O")
+    assert_close(got["lse"].cpu().numpy().astype(np.float64), ref["lse"], 1e-3, "LSE")
+    check_grads(cfg, got, ref)
+    rk, rv = _sum_rules(decode(dev_to_bits(got["dk"]))[:, 0], decode(dev_to_bits(got["dv"]))[:, 0],
+                        decode(dev_to_bits(run.packed("do"))))
+    print(f"sum rules (bf16 outputs): {rk:.3g}, {rv:.3g}")
+    assert rk < 2.5e-4 and rv < 2.5e-4
 
 
 def test_full_path_unpack_c1_and_varlen():
@@ -194,9 +217,7 @@ def test_full_path_unpack_c1_and_varlen():
             for j in range(cfg.P):
                 assert np.array_equal(dev_to_bits(shards[j]), want[j]), (name, j)
             val = decode(dev_to_bits(got[name]))
-            # bf16 values: within 2e-2 plus half an ulp (see the module docstring)
-            tol = 1e-4 if cfg.dtype == "f32" else 2e-2 + bf16_tol(ref[name], 0.0) / 2
-            assert_close(val, ref[name], tol, name)
+            assert_close(val, ref[name], tol_for(cfg, ref[name]), name)
 
 
 def test_bwd_deterministic():
@@ -243,10 +264,14 @@ def test_million_token_head_group_sampled():
     ref_tail = oracle_attention(run, rows=np.arange(tail, cfg.N))
     for name in ("dk", "dv"):
         check_grad(cfg, got, ref_tail, name, sel=slice(tail, None), ref_sel=slice(tail, None))
+    # sum rules on the fp32-output gradients, summed on the GPU in float64:
+    # the residue is rounding (about 2e-5 measured); a dropped or doubled
+    # 32-row query tile of one head moves it by 1e-6 to 1e-4 per column, so
+    # the bound is kept near the measured floor
     dk = got["dk32"][:, 0].double()
     dv = got["dv32"][:, 0].double()
     do = run.packed("do").double()
     rk = (dk.sum(0).abs() / dk.abs().sum(0)).max().item()
     rv = ((dv.sum(0) - do.sum((0, 1))).abs() / dv.abs().sum(0)).max().item()
     print(f"1M sum rules: max |sum dK|/sum|dK| = {rk:.3g}, max |sum dV - sum dO|/sum|dV| = {rv:.3g}")
-    assert rk < 1e-2 and rv < 1e-2
+    assert rk < 2e-4 and rv < 2e-4

@@ -55,6 +55,10 @@ SMALL = [
     (333, 3, 6, 3, 128, "f32", None),                          # fp32 D=128, GQA 2:1
     (64, 1, 4, 1, 64, "f32", [10, 54]),                        # one tile, fp32 D=64
     (8, 8, 8, 8, 128, "bf16", None),                           # fewer tokens than a tile
+    (1000, 4, 32, 4, 128, "bf16", None),                       # G=8: one 32-row tile, 8 heads per workgroup
+    (1536, 2, 32, 2, 128, "bf16", [700, 836]),                 # G=16: two head groups per kv head
+    (640, 1, 8, 1, 64, "bf16", [100, 1, 539]),                 # G=8, D=64
+    (512, 2, 64, 4, 128, "bf16", None),                        # G=16 over two kv heads
 ]
 
 

@@ -3,9 +3,9 @@ document sees the whole document; no causal bound) against the fp64 oracle
 with the same mask.
 
 Tolerances as for the causal kernels: fp32 max-abs <= 1e-4; bf16 O within
-max(2e-2, one bf16 ulp of |ref|), LSE within 1e-3; bf16 gradients computed
-once more with fp32 outputs, which must be within 2e-2 of the oracle, and the
-bf16 gradients equal to their round-to-nearest-even bit for bit.
+max(2e-2, one bf16 ulp of |ref|), LSE within 1e-3; bf16 gradients within
+max(2e-2, one bf16 ulp of |ref|), the same gradients with fp32 outputs within
+2e-2, and the bf16 gradients equal to their round-to-nearest-even bit for bit.
 """
 import numpy as np
 import pytest
@@ -67,6 +67,7 @@ def check(run, got, ref, rows=None, grads=True):
         else:
             g32 = got[n + "32"][sel]
             assert_close(g32.cpu().numpy().astype(np.float64), ref[n], 2e-2, n + " (fp32 out)")
+            assert_close(decode(dev_to_bits(got[n][sel])), ref[n], bf16_tol(ref[n]), n)
             assert np.array_equal(dev_to_bits(got[n][sel]), dev_to_bits(g32.to(torch.bfloat16))), n
 
 
@@ -111,7 +112,7 @@ def test_noncausal_c5_documents_sampled_rows():
             continue
         rk = np.abs(dk[a:b].sum(axis=0)) / np.abs(dk[a:b]).sum(axis=0)
         rv = np.abs(dv[a:b].sum(axis=0) - do[a:b].sum(axis=(0, 1))) / np.abs(dv[a:b]).sum(axis=0)
-        assert rk.max() < 1e-2 and rv.max() < 1e-2, (a, b, rk.max(), rv.max())
+        assert rk.max() < 1e-3 and rv.max() < 1e-3, (a, b, rk.max(), rv.max())
 
 
 def test_causal_flag_changes_only_what_it_should():

@@ -80,7 +80,7 @@ def test_document_isolation_bitwise(causal):
     assert not _same(o1[a:b], o2[a:b])
 
 
-@pytest.mark.parametrize("G", [4, 2])
+@pytest.mark.parametrize("G", [4, 2, 8, 16])
 def test_gqa_equals_repeated_kv(G):
     N, hk, D = 2048, 2, 128
     hq = hk * G
