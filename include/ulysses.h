@@ -19,6 +19,7 @@
  *   attn_bwd         its backward (dQ, dK, dV) with logsumexp recompute
  *   attn_bwd_ex      the same with float32 gradients from bf16 inputs
  *   attn_bwd_accumulate  the same, adding to the gradients (chunked attention)
+ *   attn_bwd_noalloc the same without a workspace argument (a static buffer)
  *   ulysses_unpack   head-sharded -> sequence-sharded (the inverse of pack)
  *   ulysses_pack_heads / ulysses_unpack_heads
  *                    the same for any run of heads (replicated kv heads)
@@ -347,6 +348,30 @@ uly_status attn_bwd_accumulate(const void* q, const void* k, const void* v, cons
                                int64_t N, int hq, int hk, int D, uly_dtype dt,
                                const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments as attn_bwd without the workspace; the
+ * library's own static device buffer of ULY_NOALLOC_SCRATCH_BYTES serves as
+ * workspace (each GPU the library runs on holds its copy until the process
+ * ends), and each dK/dV key block is done by one workgroup (no partial sums),
+ * so dq is bitwise the same as attn_bwd's and dk/dv differ from it only in
+ * the order of their float32 sums. The call allocates nothing and frees
+ * nothing. Sizes whose workspace exceeds the buffer return
+ * ULY_ERR_UNSUPPORTED (bf16, 4 q heads on 1 kv head, D = 128: up to 51780
+ * tokens); a stream that does not belong to the current device returns
+ * ULY_ERR_INVALID_ARG. Every call on one GPU uses the same buffer: calls that
+ * overlap in time on one GPU (on several streams, or from several host
+ * threads) race and give wrong results. Other preconditions and errors as
+ * attn_bwd.
+ */
+#define ULY_NOALLOC_SCRATCH_BYTES (128u << 20)
+uly_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            int64_t N, int hq, int hk, int D, uly_dtype dt,
+                            const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                            hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * Never NULL; valid until the next call on the same thread. */

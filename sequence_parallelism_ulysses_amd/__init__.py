@@ -15,11 +15,13 @@ from ._lib import (  # noqa: F401
     ULY_ERR_UNSUPPORTED,
     ULY_F32,
     ULY_MAX_P,
+    ULY_NOALLOC_SCRATCH_BYTES,
     ULY_OK,
     UlyssesError,
     attn_bwd,
     attn_bwd_ex,
     attn_bwd_accumulate,
+    attn_bwd_noalloc,
     attn_bwd_workspace_size,
     attn_fwd,
     attn_fwd_from_shards,

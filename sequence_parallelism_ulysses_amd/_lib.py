@@ -17,6 +17,7 @@ LIB_NAME = "libulysses.so"
 ULY_OK, ULY_ERR_INVALID_ARG, ULY_ERR_UNSUPPORTED, ULY_ERR_HIP = 0, 1, 2, 3
 ULY_F32, ULY_BF16 = 0, 1
 ULY_MAX_P = 64
+ULY_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # name -> (restype, argtypes); mirrors include/ulysses.h
 _vp = ctypes.c_void_p
@@ -47,6 +48,8 @@ SIGNATURES = {
                            _f32, _i32, _vp, ctypes.c_size_t, _vp, _i32]),
     "attn_bwd_accumulate": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
                                    _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
+                                _i32, _f32, _i32, _vp]),
     "uly_last_error": (ctypes.c_char_p, []),
     "uly_check_cu_seqlens": (_i32, [ctypes.POINTER(ctypes.c_int32), _i32, _i64]),
 }
@@ -333,6 +336,23 @@ def attn_bwd_accumulate(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float,
     import torch
     _bwd("attn_bwd_accumulate", q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal,
          stream, grad_dtype=torch.float32)
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, cu_seqlens=None, causal: int = 1,
+                     stream=None) -> None:
+    """attn_bwd with the library's static buffer as workspace: allocates
+    nothing (see include/ulysses.h)."""
+    import torch
+    N, hq, D = q.shape
+    hk = k.shape[1]
+    dt = q.dtype
+    args = [_dev(q, (N, hq, D), dt, "q"), _dev(k, (N, hk, D), dt, "k"), _dev(v, (N, hk, D), dt, "v"),
+            _dev(o, (N, hq, D), dt, "o"), _dev(dout, (N, hq, D), dt, "dout"),
+            _dev(lse, (hq, N), torch.float32, "lse"), _dev(dq, (N, hq, D), dt, "dq"),
+            _dev(dk, (N, hk, D), dt, "dk"), _dev(dv, (N, hk, D), dt, "dv")]
+    cu, nd = _cu(cu_seqlens, N)
+    _raise(lib().attn_bwd_noalloc(*args, N, hq, hk, D, _dtype_code(q), cu, nd, float(softmax_scale), int(causal),
+                                  _stream(stream)))
 
 
 def _bwd(fn, q, k, v, o, dout, lse, dq, dk, dv, softmax_scale, workspace, cu_seqlens, causal, stream, grad_dtype,

@@ -133,6 +133,7 @@ uly_status check_attn(const char* fn, int64_t N, int hq, int hk, int D, int dt,
   d->scale = scale;
   d->causal = causal;
   d->accumulate = 0;
+  d->splits = 0;
   return ULY_OK;
 }
 
@@ -450,6 +451,32 @@ uly_status attn_bwd_accumulate(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return bwd_common("attn_bwd_accumulate", 1, q, k, v, o, dout, lse, dq, dk, dv, N, hq, hk, D, dt, cu_seqlens,
                     ndocs, softmax_scale, causal, workspace, workspace_bytes, stream, ULY_F32);
+}
+
+uly_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, int64_t N, int hq, int hk, int D,
+                            uly_dtype dt, const int32_t* cu_seqlens, int ndocs, float softmax_scale, int causal,
+                            hipStream_t stream) {
+  const char* fn = "attn_bwd_noalloc";
+  uly::AttnDesc d;
+  uly_status s = check_attn(fn, N, hq, hk, D, dt, cu_seqlens, ndocs, softmax_scale, causal, &d);
+  if (s != ULY_OK) return s;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i)
+    CHECK(ptrs[i] != nullptr && aligned16(ptrs[i]), ULY_ERR_INVALID_ARG,
+          "%s: %s is NULL or not 16-byte aligned", fn, names[i]);
+  uly::AttnDesc one = d;
+  one.splits = 1;
+  const size_t need = uly::bwd_workspace_bytes(one);
+  CHECK(need <= uly::kNoAllocScratchBytes, ULY_ERR_UNSUPPORTED,
+        "%s: these sizes need %zu bytes of workspace, more than the %zu bytes of the static buffer", fn, need,
+        uly::kNoAllocScratchBytes);
+  size_t need2 = 0;
+  const hipError_t e = uly::launch_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, d, stream, &need2);
+  if (e == hipErrorInvalidDevice)
+    return fail(ULY_ERR_INVALID_ARG, "%s: the stream does not belong to the current device", fn);
+  return from_hip(e, fn);
 }
 
 }  // extern "C"

@@ -54,7 +54,7 @@ constexpr int kKeysPerWg = 32 * kWaves;
 // split order by dkdv_reduce_kernel. Timed over 1, 2, 3, 4, 6 and 8 at 32k,
 // 128k and 256k tokens (Llama-3.1-8B-shaped head group), 4 was fastest at
 // every size (by 0.5-3 %).
-int dkdv_splits(const AttnDesc&) { return 4; }
+int dkdv_splits(const AttnDesc& d) { return d.splits > 0 ? d.splits : 4; }
 
 struct WsLayout {
   size_t delta, lse2, absmax, q16, do16, k16, v16, part, total;

@@ -39,6 +39,7 @@ struct AttnDesc {
   float scale;
   int causal;            // 1: key j visible to query i iff j <= i (and same document); 0: same document
   int accumulate;        // backward only: add to dq, dk, dv (fp32 gradients) instead of overwriting
+  int splits;            // backward only: workgroups per dK/dV key block (0: the default)
 };
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -55,6 +56,14 @@ hipError_t launch_attn_merge(const void* const* o_parts, const float* const* lse
                              int hq, int D, uly_dtype dt, void* o, float* lse, hipStream_t stream);
 
 size_t bwd_workspace_bytes(const AttnDesc& d);
+// attn_bwd with the library's own static device buffer as workspace (one
+// workgroup per dK/dV key block, so that no partial sums need space).
+// Returns hipErrorInvalidValue without launching when the sizes need more
+// than kNoAllocScratchBytes (*need is then set).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t launch_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   const AttnDesc& d, hipStream_t stream, size_t* need);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            void* workspace, const AttnDesc& d, uly_dtype grad_dt, hipStream_t stream);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_ex", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_from_shards", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
+        "attn_bwd", "attn_bwd_accumulate", "attn_bwd_ex", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_from_shards", "attn_merge", "uly_check_cu_seqlens", "uly_last_error",
         "ulysses_pack", "ulysses_pack_heads", "ulysses_pack_multi", "ulysses_pack_qkv", "ulysses_unpack",
         "ulysses_unpack_heads", "ulysses_unpack_multi", "ulysses_unpack_qkv"])
 
@@ -393,11 +393,44 @@ def test_boundary_prototype_matches(name):
 
 def test_extended_backward_calls_extend_the_boundary_list():
     """attn_bwd_ex is attn_bwd's list plus grad_dt at the end;
-    attn_bwd_accumulate has exactly attn_bwd's list."""
+    attn_bwd_accumulate has exactly attn_bwd's list; attn_bwd_noalloc has it
+    without the workspace."""
     protos = declared_prototypes()
     base = protos["attn_bwd"][1]
     assert protos["attn_bwd_ex"][1] == base + [("uly_dtype", "grad_dt")]
     assert protos["attn_bwd_accumulate"][1] == base
+    assert protos["attn_bwd_noalloc"][1] == [p for p in base if p[1] not in ("workspace", "workspace_bytes")]
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, N=1024, hq=4, hk=1,
+             D=128, dt=uly.ULY_BF16, cu=None, nd=0, scale=0.088, causal=1, stream=None)
+    a.update(kw)
+    return uly.lib().attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                      a["N"], a["hq"], a["hk"], a["D"], a["dt"], a["cu"], a["nd"], a["scale"],
+                                      a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dq=None), uly.ULY_ERR_INVALID_ARG, "dq is NULL"),
+    (dict(o=FAKE + 4), uly.ULY_ERR_INVALID_ARG, "o is NULL or not"),
+    (dict(hk=3), uly.ULY_ERR_INVALID_ARG, "multiple"),
+    (dict(causal=3), uly.ULY_ERR_INVALID_ARG, "causal=3"),
+    # the static buffer holds the workspace of up to 51780 tokens at 4 q heads
+    # on 1 kv head, D = 128, bf16
+    (dict(N=51781), uly.ULY_ERR_UNSUPPORTED, "static buffer"),
+    (dict(N=1 << 20), uly.ULY_ERR_UNSUPPORTED, "static buffer"),
+])
+def test_attn_bwd_noalloc_rejects(kw, status, needle):
+    assert _noalloc(**kw) == status
+    assert needle in uly.last_error() and "attn_bwd_noalloc" in uly.last_error()
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ULY_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == uly.ULY_NOALLOC_SCRATCH_BYTES
+    assert "up to 51780" in text
 
 
 _SCALAR = {"int": ctypes.c_int, "uly_dtype": ctypes.c_int, "int64_t": ctypes.c_int64, "size_t": ctypes.c_size_t,
