@@ -47,6 +47,9 @@ def causal_pairs(N: int, cu) -> int:
 
 
 def oracle_threads() -> int:
+    """Threads for the oracle: every core this process may run on, capped at
+    16, the CPU share of one GPU on the boxes this runs on (the host itself
+    may show more cores; they belong to the other GPUs' jobs)."""
     n = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
@@ -54,10 +57,11 @@ def oracle_threads() -> int:
     return max(1, min(n, 16))
 
 
-def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
+def cpu_baseline(cfg, cu, host, budget_s: float):
     """The oracle as it stands, on a bounded sample of the same workload: fp64
     forward+backward for the last R query rows of the head group (every
-    visible key), R sized to take about `budget_s` seconds."""
+    visible key), R sized to take about `budget_s` seconds. Returns the
+    record and the oracle's result for those rows."""
     from oracle import attn_ref, bf16_bits_to_f64, f32_bits_to_f64, pack_ref
 
     dec = bf16_bits_to_f64 if cfg.dtype == "bf16" else f32_bits_to_f64
@@ -68,26 +72,55 @@ def cpu_baseline(cfg, cu, host, budget_s: float) -> dict:
     def run(R):
         rows = np.arange(cfg.N - R, cfg.N)
         t = time.perf_counter()
-        attn_ref(x["q"], x["k"], x["v"], cfg.scale, cu, do=x["do"], rows=rows, workers=workers)
+        res = attn_ref(x["q"], x["k"], x["v"], cfg.scale, cu, do=x["do"], rows=rows, workers=workers)
         dt = time.perf_counter() - t
         pairs = int((rows - start[rows] + 1).sum())
-        return dt, pairs
+        return dt, pairs, res
 
     # probe, then size R so that the measured run takes about budget_s (the
     # cost of a row is about proportional to the keys it sees)
     R = min(cfg.N, 64)
-    dt, pairs = run(R)
+    dt, pairs, res = run(R)
     while dt < budget_s / 2 and R < cfg.N:
         R = min(cfg.N, int(R * max(1.5, min(8.0, budget_s / max(dt, 1e-3)))))
-        dt, pairs = run(R)
+        dt, pairs, res = run(R)
     flops = 14 * cfg.D * cfg.hq * pairs
     rate = flops / dt
     full = 14 * cfg.D * cfg.hq * causal_pairs(cfg.N, cu)
-    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"fp64 numpy oracle, forward+backward of the last {R} query rows x {cfg.hq} q heads "
-                      f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}",
-            "full_step_seconds_extrapolated": round(full / rate, 1)}
+    rec = {"value": rate / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "host_cores": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+           "seconds": round(dt, 2),
+           "sample": f"fp64 numpy oracle, forward+backward of the last {R} query rows x {cfg.hq} q heads "
+                     f"({pairs * cfg.hq:.3g} causal pairs) of workload {cfg.workload}",
+           "full_step_seconds_extrapolated": round(full / rate, 1)}
+    return rec, res
+
+
+def parity_of_sample(outs, res, N: int) -> dict:
+    """The timed step's outputs against the oracle on the sampled rows: O,
+    LSE and dQ of those rows, and dK/dV of the key columns from the first
+    sampled row on (only rows at or after a key see it, so the oracle's sums
+    over the sampled rows are complete there). Max-abs errors, max |ref|, and
+    the worst error relative to max(2e-2, one bf16 ulp of |ref|)."""
+    import torch
+    rows = res["rows"]
+    lo = int(rows[0])
+    sel = torch.from_numpy(rows).to(outs["o"].device)
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+    pairs = {"o": (f64(outs["o"][sel]), res["o"]), "lse": (f64(outs["lse"][:, sel]), res["lse"]),
+             "dq": (f64(outs["dq"][sel]), res["dq"]), "dk": (f64(outs["dk"][lo:]), res["dk"][lo:]),
+             "dv": (f64(outs["dv"][lo:]), res["dv"][lo:])}
+    out = {}
+    for name, (got, ref) in pairs.items():
+        err = np.abs(got - ref)
+        bar = np.maximum(2e-2, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7))
+        out[name] = {"max_err": float(err.max()), "max_abs_ref": float(np.abs(ref).max())}
+        if name != "lse":
+            out[name]["worst_err_over_bar"] = round(float((err / bar).max()), 4)
+    out["elements"] = f"rows {lo}..{N - 1} of O, LSE, dQ; key columns {lo}..{N - 1} of dK, dV"
+    return out
 
 
 # The sources of the attn_bwd call's kernels (and what they include).
@@ -399,7 +432,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": cfg.workload, "N": N, "P": P, "tokens_per_shard": T, "q_heads": hq, "kv_heads": hk,
                    "head_dim": D, "causal": True, "documents": None if cu is None else int(len(cu) - 1),
-                   "causal_pairs": C, "step_flop": step_flop},
+                   "causal_pairs": C, "step_flop": step_flop,
+                   "seed": f"numpy SeedSequence({cfg.seed}), one child per tensor (q, k, v, dO) and shard"},
         "frac_mfma_step": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "pack_unpack": {"GB/s": round(pack_total_bytes / (pack_total_ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(pack_total_bytes / (pack_total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -416,7 +450,8 @@ def main() -> int:
         line["chunked"] = chunked_rates(uly, cfg, qg, kg, vg, dog, fwd_flop, bwd_flop, call_ms,
                                         max(3, args.steps // 4))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, cu, host, args.cpu_seconds)
+        line["cpu_baseline"], res = cpu_baseline(cfg, cu, host, args.cpu_seconds)
+        line["parity_sample"] = parity_of_sample({"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, res, N)
     print(json.dumps(line), flush=True)
     return 0
 

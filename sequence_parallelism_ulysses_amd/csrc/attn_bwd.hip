@@ -47,45 +47,6 @@ constexpr int kWaves = 4;
 
 constexpr int kKeysPerWg = 32 * kWaves;
 
-// Workgroups per dK/dV key tile. Each key block's (query tile, head)
-// iterations are dealt round-robin to this many workgroups, which then stream
-// the same Q/dO tiles at about the same time (shared in L2) and balance the
-// causal spread of work per key block; their fp32 partials are added in
-// split order by dkdv_reduce_kernel. Timed over 1, 2, 3, 4, 6 and 8 at 32k,
-// 128k and 256k tokens (Llama-3.1-8B-shaped head group), 4 was fastest at
-// every size (by 0.5-3 %).
-int dkdv_splits(const AttnDesc& d) { return d.splits > 0 ? d.splits : 4; }
-
-struct WsLayout {
-  size_t delta, lse2, absmax, q16, do16, k16, v16, part, total;
-};
-WsLayout ws_layout(const AttnDesc& d) {
-  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  WsLayout w;
-  const size_t row_bytes = up(size_t(4) * d.hq * d.N);
-  w.delta = 0;
-  w.lse2 = row_bytes;
-  size_t at = 2 * row_bytes;
-  if (d.dt == ULY_BF16) {
-    // the maxima (kMaxSlots uint32), then the fp16 operand copies
-    w.absmax = at;
-    at += up(kMaxSlots * 4);
-    const size_t qb = up(size_t(2) * d.N * d.hq * d.D), kb = up(size_t(2) * d.N * d.hk * d.D);
-    w.q16 = at;
-    w.do16 = at + qb;
-    w.k16 = at + 2 * qb;
-    w.v16 = at + 2 * qb + kb;
-    at += 2 * qb + 2 * kb;
-  } else {
-    w.absmax = w.q16 = w.do16 = w.k16 = w.v16 = 0;
-  }
-  w.part = at;
-  const int s = dkdv_splits(d);
-  const size_t part_bytes = s > 1 ? size_t(2) * s * d.N * d.hk * d.D * 4 : 0;
-  w.total = w.part + part_bytes;
-  return w;
-}
-
 __device__ __forceinline__ u32x4_t ld16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
 // ----------------------------------------------------------------------------
@@ -834,10 +795,10 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   p.dq = static_cast<char*>(dq);
   p.dk = static_cast<char*>(dk);
   p.dv = static_cast<char*>(dv);
-  const WsLayout wl = ws_layout(d);
+  const BwdWorkspace wl = bwd_workspace_layout(d);
   p.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.delta);
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse2);
-  p.splits = dkdv_splits(d);
+  p.splits = bwd_dkdv_splits(d);
   char* ws = static_cast<char*>(workspace);
   const bool half_ops = Tr::kElem == 2;  // bf16 inputs: fp16 operand copies (BwdScales)
   p.absmax = half_ops ? reinterpret_cast<uint32_t*>(ws + wl.absmax) : nullptr;
@@ -906,8 +867,6 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
 }
 
 }  // namespace
-
-size_t bwd_workspace_bytes(const AttnDesc& d) { return ws_layout(d).total; }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, void* dq, void* dk, void* dv, void* workspace, const AttnDesc& d,

@@ -66,7 +66,7 @@ struct BwdScales {
 // Slots of the maxima in the workspace (uint32 index, 256 bytes apart):
 // max |x| as bf16 bits for q, k, v, dout, then the largest squared row norm
 // (fp32 bits) of dout and v.
-enum { kMaxQ = 0, kMaxK = 64, kMaxV = 128, kMaxDo = 192, kNormDo = 256, kNormV = 320, kMaxSlots = 384 };
+enum { kMaxQ = 0, kMaxK = 64, kMaxV = 128, kMaxDo = 192, kNormDo = 256, kNormV = 320, kMaxSlots = kBwdMaxima };
 
 // Exponent bound of a bf16 |value| bit pattern: |x| < 2^k. Zero and
 // subnormals give -126; inf/NaN give 0 (the results are not finite anyway).

@@ -55,6 +55,17 @@ hipError_t launch_attn_fwd_from_shards(const void* const* q_shards, const void* 
 hipError_t launch_attn_merge(const void* const* o_parts, const float* const* lse_parts, int nparts, int64_t N,
                              int hq, int D, uly_dtype dt, void* o, float* lse, hipStream_t stream);
 
+// Workspace of the backward (workspace.cpp): per-row delta and lse*log2(e)
+// (float32 [hq][N] each); for bf16 inputs the maxima the fp16 operand
+// scales derive from (kBwdMaxima uint32 slots) and the fp16 copies of q,
+// dout ([N][hq][D]) and k, v ([N][hk][D]); the float32 partial dK/dV sums of
+// the workgroups sharing a key block when there are several.
+constexpr int kBwdMaxima = 384;
+struct BwdWorkspace {
+  size_t delta, lse2, absmax, q16, do16, k16, v16, part, total;
+};
+int bwd_dkdv_splits(const AttnDesc& d);
+BwdWorkspace bwd_workspace_layout(const AttnDesc& d);
 size_t bwd_workspace_bytes(const AttnDesc& d);
 // attn_bwd with the library's own static device buffer as workspace (one
 // workgroup per dK/dV key block, so that no partial sums need space).
