@@ -211,13 +211,17 @@ struct KvCfg {
   static constexpr int E = Tr::kElem;
   static constexpr int KS = D / Tr::kStep;   // MFMA steps over D
   static constexpr int DB = D / 32;
-  static constexpr int QS = BT / Tr::kStep;  // MFMA steps over the 64 queries of a tile
+  // query rows per tile: 32 for D = 128, whose K/V rows and dK/dV
+  // accumulators already take 256 registers per lane (64 would spill)
+  static constexpr int QT = D == 128 ? 32 : 64;
+  static constexpr int QB = QT / 32;          // 32-row blocks per tile
+  static constexpr int QS = QT / Tr::kStep;   // MFMA steps over the queries of a tile
   // tiles are row-major with a 16-byte pad per row; transposed operands are
   // read element by element from them
   static constexpr int F_STRIDE = D * 4 + 16;
-  static constexpr int X_BYTES = BT * F_STRIDE;           // one tile
-  static constexpr int STAGE = 2 * X_BYTES + 2 * BT * 4;  // Q, dO, lse2, delta
-  static constexpr int F_CH = BT * D * 4 / 16 / kThreads;  // 16-byte chunks per thread
+  static constexpr int X_BYTES = QT * F_STRIDE;           // one tile
+  static constexpr int STAGE = 2 * X_BYTES + 2 * QT * 4;  // Q, dO, lse2, delta
+  static constexpr int F_CH = QT * D * 4 / 16 / kThreads;  // 16-byte chunks per thread
 };
 
 template <class Tr, int D>
@@ -240,7 +244,7 @@ struct QTile {
       xq[i] = ok ? ld16(qb + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
       xd[i] = ok ? ld16(db + q * row_bytes + col * 16) : u32x4_t{0, 0, 0, 0};
     }
-    if (tid < BT) {
+    if (tid < C::QT) {
       const int q = qs + tid;
       lse2 = q < p.N ? p.lse[int64_t(head) * p.N + q] * kLog2e : 0.f;
       dlt = q < p.N ? p.delta[int64_t(head) * p.N + q] : 0.f;
@@ -258,9 +262,9 @@ struct QTile {
       *reinterpret_cast<u32x4_t*>(qr + row * C::F_STRIDE + col * 16) = xq[i];
       *reinterpret_cast<u32x4_t*>(dr + row * C::F_STRIDE + col * 16) = xd[i];
     }
-    if (tid < BT) {
+    if (tid < C::QT) {
       fl[tid] = lse2;
-      fl[BT + tid] = dlt;
+      fl[C::QT + tid] = dlt;
     }
   }
 };
@@ -303,13 +307,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
   // head-major, are split evenly between p.splits workgroups; this one takes
   // [it0, it1).
   const int q_end = doc_of(p.cu, p.ndocs, p.N, min(kv0 + 32 * kWaves - 1, p.N - 1)).end;
-  const int qt0 = first_query(p, kv0) / BT;
-  const int n_qt = (q_end - 1) / BT - qt0 + 1;
+  const int qt0 = first_query(p, kv0) / C::QT;
+  const int n_qt = (q_end - 1) / C::QT - qt0 + 1;
   const int n_it = n_qt * p.G;
   const int it0 = int(int64_t(n_it) * split / p.splits);
   const int it1 = int(int64_t(n_it) * (split + 1) / p.splits);
   auto head_of = [&](int it) { return kvh * p.G + it / n_qt; };
-  auto qs_of = [&](int it) { return (qt0 + it % n_qt) * BT; };
+  auto qs_of = [&](int it) { return (qt0 + it % n_qt) * C::QT; };
 
   QTile<Tr, D> tile;
   if (it0 < it1) {
@@ -317,7 +321,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
     tile.store(smem, tid);
   }
   __syncthreads();
-  if (it0 + 1 < it1) tile.load(p, head_of(it0 + 1), qs_of(it0 + 1), tid);
+  // 64-row tiles: the next tile is loaded into registers during this one's
+  // products; 32-row tiles (D = 128, no registers to spare): at its end
+  constexpr bool kPrefetch = C::QT == 64;
+  if (kPrefetch && it0 + 1 < it1) tile.load(p, head_of(it0 + 1), qs_of(it0 + 1), tid);
 
   for (int it = it0; it < it1; ++it) {
     const int qs = qs_of(it);
@@ -326,14 +333,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
     const char* dr = st + C::X_BYTES;
     const float* fl = reinterpret_cast<const float*>(st + 2 * C::X_BYTES);
 
-    if (active && qs + BT - 1 >= kbd.w_lo_first && qs < w_de_last) {
-      f32x16_t s[2], dp[2];
+    if (active && qs + C::QT - 1 >= kbd.w_lo_first && qs < w_de_last) {
+      f32x16_t s[C::QB], dp[C::QB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = f32x16_t{};
+      for (int qb = 0; qb < C::QB; ++qb) s[qb] = dp[qb] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < C::QB; ++qb) {
           const int row = qb * 32 + l32;
           const frag_t a = load_frag<Tr>(qr + row * C::F_STRIDE + (2 * ks + half) * 4);
           const frag_t b = load_frag<Tr>(dr + row * C::F_STRIDE + (2 * ks + half) * 4);
@@ -341,15 +348,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
           dp[qb] = mfma(b, vf[ks], dp[qb]);
         }
       }
-      const bool need_mask = (qs < kbd.w_lo_last) || (qs + BT > w_de_first);
-      float pv[32], dsv[32];
+      const bool need_mask = (qs < kbd.w_lo_last) || (qs + C::QT > w_de_first);
+      float pv[16 * C::QB], dsv[16 * C::QB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int qi = qb * 32 + 8 * r4 + 4 * half;  // first of 4 consecutive queries
           const float4 l4 = *reinterpret_cast<const float4*>(fl + qi);
-          const float4 d4 = *reinterpret_cast<const float4*>(fl + BT + qi);
+          const float4 d4 = *reinterpret_cast<const float4*>(fl + C::QT + qi);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -382,8 +389,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
     }
 
     if (it + 1 < it1) {
+      if (!kPrefetch) tile.load(p, head_of(it + 1), qs_of(it + 1), tid);
       tile.store(smem + ((it + 1 - it0) & 1) * C::STAGE, tid);
-      if (it + 2 < it1) tile.load(p, head_of(it + 2), qs_of(it + 2), tid);
+      if (kPrefetch && it + 2 < it1) tile.load(p, head_of(it + 2), qs_of(it + 2), tid);
     }
     __syncthreads();
   }
