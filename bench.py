@@ -124,7 +124,8 @@ def parity_of_sample(outs, res, N: int) -> dict:
 
 
 # The sources of the attn_bwd call's kernels (and what they include).
-BWD_SOURCES = ("attn_bwd.hip", "attn_bwd_dkdv.hip", "bwd_common.hpp", "lds_tile.hpp", "common.hpp", "internal.hpp")
+BWD_SOURCES = ("attn_bwd.hip", "attn_bwd_dkdv.hip", "bwd_common.hpp", "lds_tile.hpp", "common.hpp", "internal.hpp",
+               "workspace.cpp")
 
 
 def source_digest() -> str:
@@ -406,7 +407,7 @@ def main() -> int:
     dom_flop = bwd_flop if dom == "attn_bwd" else fwd_flop
     achieved = dom_flop / (call_ms[dom] * 1e-3) / 1e12
     roofline = {
-        "kernel": dom + (" (delta + dkdv + dq launches)" if dom == "attn_bwd" else ""),
+        "kernel": dom + (" (prep + convert + dK/dV + reduce + dQ launches)" if dom == "attn_bwd" else ""),
         "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "traffic": measured_traffic(cfg.workload) if dom == "attn_bwd" else None,
