@@ -91,16 +91,34 @@ void dkdv_bf16_kernel(BwdParams p) {
   const int it0 = 0;
   const int it1 = max(0, (n_it - split + p.splits - 1) / p.splits);
 
-  auto tile_q0 = [&](int it) { return (qt0 + n_qt - 1 - (split + it * p.splits) / p.G) * C::QT; };
-  auto tile_head = [&](int it) { return kvh * p.G + (split + it * p.splits) % p.G; };
+  // Local iteration it is the (query tile, head) pair number split + it *
+  // splits = qi * G + hi of the key block's walk. Each wave keeps cursors
+  // (qi, hi) and advances them by additions, rather than dividing by G on
+  // every iteration (a division is a long chain of scalar instructions on
+  // each wave's critical path).
+  struct Cursor {
+    int qi, hi;
+  };
+  const int step_q = p.splits / p.G, step_h = p.splits % p.G;
+  const Cursor first{split / p.G, split % p.G};
+  auto advance = [&](Cursor& c) {
+    c.qi += step_q;
+    c.hi += step_h;
+    if (c.hi >= p.G) {
+      c.hi -= p.G;
+      ++c.qi;
+    }
+  };
+  auto tile_q0 = [&](const Cursor& c) { return (qt0 + n_qt - 1 - c.qi) * C::QT; };
+  auto tile_head = [&](const Cursor& c) { return kvh * p.G + c.hi; };
   auto stage = [&](int it) { return ring + ((it - it0) % C::NSTAGE) * C::STAGE; };
   // does a key block (first key kb0, seen from query lo_first on, its
-  // documents ending by de_last) receive gradient from tile it?
-  auto sees_block = [&](int it, int kb0, int lo_first, int de_last) {
-    const int qs = tile_q0(it);
+  // documents ending by de_last) receive gradient from the tile at c?
+  auto sees_block = [&](const Cursor& c, int kb0, int lo_first, int de_last) {
+    const int qs = tile_q0(c);
     return kb0 < p.N && qs + C::QT - 1 >= lo_first && qs < de_last;
   };
-  auto sees = [&](int it) { return sees_block(it, kw0, kbd.w_lo_first, w_de_last); };
+  auto sees = [&](const Cursor& c) { return sees_block(c, kw0, kbd.w_lo_first, w_de_last); };
   // P (slots 0, 1) and dS (slots 2, 3) fragments of tile it for key block b
   auto pds_at = [&](int it, int b, int slot) {
     return pds + (((it & 1) * 4 + b) * 4 + slot) * 1024 + lane * 16;
@@ -121,10 +139,11 @@ void dkdv_bf16_kernel(BwdParams p) {
     RowFragOffsets<D> ro;  // rows l%32 of a tile, k = 16 ks + 8 half
     ro.init(lane);
 
-    for (int it = it0; it <= it1; ++it) {
+    Cursor cur = first;  // at iteration it
+    for (int it = it0; it <= it1; ++it, advance(cur)) {
       __syncthreads();  // tile it has landed (the consumers waited for it)
-      if (it < it1 && sees(it)) {
-        const int qs = tile_q0(it);
+      if (it < it1 && sees(cur)) {
+        const int qs = tile_q0(cur);
         const lds_char* qt = stage(it);
         const lds_char* dt = qt + C::TQ;
         typedef __attribute__((address_space(3))) const float lds_float;
@@ -209,10 +228,10 @@ void dkdv_bf16_kernel(BwdParams p) {
   TrFragOffsets<D> to;  // transposed reads over 16-row steps
   to.init(lane);
   const int ctid = tid - C::kProducers;
-  auto issue = [&](int it) {
+  auto issue = [&](int it, const Cursor& c) {
     lds_char* st = stage(it);
-    const int head = tile_head(it);
-    const int qs = tile_q0(it);
+    const int head = tile_head(c);
+    const int qs = tile_q0(c);
     const int rows = min(C::QT, p.N - qs);
     const int64_t off = (int64_t(qs) * p.hq + head) * D * 2;
     issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.q16 + off, uint32_t(rows) * q_row), q_row, st, ctid);
@@ -223,8 +242,12 @@ void dkdv_bf16_kernel(BwdParams p) {
     dma_to_lds<4>(make_rsrc_uniform(p.lse2 + foff, uint32_t(rows) * 4), st + 2 * C::TQ, lane * 4);
     dma_to_lds<4>(make_rsrc_uniform(p.delta + foff, uint32_t(rows) * 4), st + 2 * C::TQ + 256, lane * 4);
   };
-  if (it0 < it1) issue(it0);
-  if (it0 + 1 < it1) issue(it0 + 1);
+  Cursor c_issue = first;  // at the tile to copy next
+  if (it0 < it1) issue(it0, c_issue);
+  advance(c_issue);
+  if (it0 + 1 < it1) issue(it0 + 1, c_issue);
+  advance(c_issue);
+  Cursor c_jt = first;  // at the tile the consumers process next
   const int slot0 = dk_role ? 2 : 0;          // dS or P fragments
   const int src_off = dk_role ? 0 : C::TQ;    // Q or dO tile
   for (int it = it0; it <= it1; ++it) {
@@ -232,9 +255,13 @@ void dkdv_bf16_kernel(BwdParams p) {
     if (it + 1 < it1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
     __syncthreads();
     // the stage of tile it-2 is free: its consumer pass ended last iteration
-    if (it + 2 < it1) issue(it + 2);
+    if (it + 2 < it1) issue(it + 2, c_issue);
+    advance(c_issue);
     const int jt = it - 1;  // the tile the producers finished last iteration
-    if (jt >= it0 && (sees_block(jt, cb_k0[0], cb_lo[0], cb_de[0]) || sees_block(jt, cb_k0[1], cb_lo[1], cb_de[1]))) {
+    const bool run = jt >= it0 && (sees_block(c_jt, cb_k0[0], cb_lo[0], cb_de[0]) ||
+                                   sees_block(c_jt, cb_k0[1], cb_lo[1], cb_de[1]));
+    if (jt >= it0) advance(c_jt);
+    if (run) {
       const lds_char* src = stage(jt) + src_off;
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2) {
