@@ -18,6 +18,9 @@ Prints one JSON line.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3] [--no-side-legs]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
                                              scaling rocprofv3 byte counters)
+       python bench.py --gemm-calibration   (the vendor library's bf16 and fp16
+                                             GEMMs, the matrix-unit rate that
+                                             this box sustains)
 """
 from __future__ import annotations
 
@@ -171,6 +174,41 @@ def copy_calibration() -> int:
     return 0
 
 
+def gemm_rates(sizes=(8192, 16384), dtypes=("bf16", "fp16")) -> dict:
+    """TFLOP/s of the vendor library's dense square GEMM (torch.matmul on
+    contiguous operands, i.e. hipBLASLt) on this GPU: the matrix-unit rate
+    that the chip sustains under a pure MFMA load, a practical ceiling to read
+    the attention kernels' rate against (the published peak assumes the
+    nominal 2.4 GHz clock, which the chip does not hold under such a load)."""
+    import torch
+    out = {}
+    gen = torch.Generator(device="cuda:0").manual_seed(0)
+    for name in dtypes:
+        dt = torch.bfloat16 if name == "bf16" else torch.float16
+        for n in sizes:
+            a = torch.randn(n, n, device="cuda:0", dtype=dt, generator=gen)
+            b = torch.randn(n, n, device="cuda:0", dtype=dt, generator=gen)
+            reps = max(3, int(2 ** 36 // n ** 3 * 8))
+            for _ in range(3):
+                c = a @ b
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[f"{name}_n{n}"] = {"ms": round(ms, 4), "tflops": round(2.0 * n ** 3 / ms / 1e9, 1)}
+            del a, b, c
+    return out
+
+
+def gemm_calibration() -> int:
+    print(json.dumps({"gemm_calibration": gemm_rates()}), flush=True)
+    return 0
+
+
 def fused_qkv_rates(uly, cfg, reps: int) -> dict:
     """The fused-projection variants of the redistribution on this workload's
     shapes: ulysses_pack_qkv from [T, Hq + 2*Hkv, D] shards into the group's
@@ -303,9 +341,12 @@ def main() -> int:
     ap.add_argument("--no-side-legs", action="store_true",
                     help="skip the fused-QKV and chunked-forward measurements (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--gemm-calibration", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
+    if args.gemm_calibration:
+        return gemm_calibration()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the path on a single GPU; "
@@ -447,6 +488,11 @@ def main() -> int:
         if cfg.T % 64 == 0:
             line["fwd_from_shards"] = fwd_from_shards_rate(uly, cfg, shards, cu_dev, fwd_flop,
                                                            call_ms["pack_qkv"] + call_ms["attn_fwd"], args.steps)
+    if not args.no_side_legs:
+        # the same box's vendor bf16 GEMM, as a practical matrix-unit ceiling
+        g = gemm_rates(dtypes=("bf16",))
+        best = max(v["tflops"] for v in g.values())
+        line["vendor_gemm"] = dict(g, step_over_best=round(value / best, 4))
     if cu is None and not args.no_side_legs:
         line["chunked"] = chunked_rates(uly, cfg, qg, kg, vg, dog, fwd_flop, bwd_flop, call_ms,
                                         max(3, args.steps // 4))
