@@ -12,15 +12,16 @@
 //
 // Three kernels, all deterministic (no atomics):
 //   1. delta: one row dot product per (query, head), and lse * log2(e).
-//   2. dK/dV, key-stationary: a workgroup owns 128 keys of one kv head, walks
-//      the query tiles that can see them for every q head of the group, and
-//      sums the GQA heads in its accumulators:
+//   2. dK/dV, key-stationary: a workgroup owns a block of keys of one kv
+//      head (fp32: 128, bf16: 192), walks the query tiles that can see them
+//      for every q head of the group, and sums the GQA heads in its
+//      accumulators:
 //        S  = Q K^T, dP = dO V^T   (A operand: Q/dO rows from LDS)
 //        dV^T += dO^T P, dK^T += Q^T dS   (A operand: transposed Q/dO tiles)
 //      The S/dP accumulators hold one key column per lane, which is the
 //      B-operand layout the second pair of products needs. fp32 (this file):
 //      4 waves of 32 keys, each doing all four products, on 64-query tiles.
-//      bf16 (attn_bwd_dkdv.hip): 8 waves on 32-query tiles, split into
+//      bf16 (attn_bwd_dkdv.hip): 12 waves on 32-query tiles, split into
 //      producers (S, dP, P, dS) and consumers (dV or dK) that pass P and dS
 //      through LDS. With splits > 1 several workgroups share a key block and
 //      write fp32 partials that dkdv_reduce_kernel adds in split order.
@@ -845,10 +846,10 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  p.n_tiles = static_cast<int>((d.N + kKeysPerWg - 1) / kKeysPerWg);
   if constexpr (Tr::kElem == 2)
-    e = launch_dkdv_bf16<D, kF32Out>(p, dim3(p.n_tiles * p.splits, d.hk), stream);
+    e = launch_dkdv_bf16<D, kF32Out>(p, p.splits, d.hk, stream);
   else {
+    p.n_tiles = static_cast<int>((d.N + kKeysPerWg - 1) / kKeysPerWg);
     dkdv_kernel<Tr, D, kF32Out><<<dim3(p.n_tiles * p.splits, d.hk), kThreads, 0, stream>>>(p);
     e = hipGetLastError();
   }

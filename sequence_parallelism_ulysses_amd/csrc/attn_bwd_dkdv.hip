@@ -1,24 +1,29 @@
 // Key-stationary dK/dV kernel for bf16 inputs (see attn_bwd.hip for the
 // backward as a whole).
 //
-// A workgroup owns 128 keys of one kv head and walks the (q head, 32-query
-// tile) iterations that can see them (split between p.splits workgroups).
-// Its 8 waves specialise in pairs that share a 32-key block kb and a SIMD:
-//   producer wave kb (0-3):  S = Q K^T and dP = dO V^T (A: Q / dO rows from
-//       the staged tile, B: this lane's K and V rows, held in registers),
-//       then P = exp(S - LSE) and dS = P (dP - Delta) on the vector unit;
-//       P and dS go to LDS as ready-made MFMA B fragments;
-//   consumer waves 4-7:      wave 4 + 2j + r accumulates dV^T += dO^T P
-//       (r = 0) or dK^T += Q^T dS (r = 1) for the 64 keys of blocks 2j and
-//       2j + 1 (A: ds_read_b64_tr_b16 of the staged dO / Q tile, each read
-//       feeding both blocks; B: the fragments), one tile behind the
-//       producers, accumulating in registers.
-// So while one wave of a SIMD is busy with exponentials the other has matrix
-// work, and neither needs registers for both the K/V rows and the dK/dV
-// accumulators. The consumers also issue the tile copies (a four-stage ring,
-// one barrier per tile): a burst of copies stalls the issuing wave at the
-// address unit, and right after the barrier the consumer has nothing urgent
-// (its products would only compete with the producer's for the matrix unit).
+// A workgroup owns 32 kP keys of one kv head (kP = 6 in use: 192 keys) and
+// walks the (q head, 32-query tile) iterations that can see them (split
+// between p.splits workgroups). Its 2 kP waves (three per SIMD) specialise:
+//   producer wave kb (0 .. kP-1): S = Q K^T and dP = dO V^T for the 32-key
+//       block kb (A: Q / dO rows from the staged tile, B: this lane's K and
+//       V rows, held in registers), then P = exp(S - LSE) and
+//       dS = P (dP - Delta) on the vector unit; P and dS go to LDS as
+//       ready-made MFMA B fragments;
+//   consumer wave kP + 2j + r: accumulates dV^T += dO^T P (r = 0) or
+//       dK^T += Q^T dS (r = 1) for the 64 keys of blocks 2j and 2j + 1
+//       (A: ds_read_b64_tr_b16 of the staged dO / Q tile, each read feeding
+//       both blocks; B: the fragments), one tile behind the producers,
+//       accumulating in registers.
+// So while one wave of a SIMD is busy with exponentials another has matrix
+// work, and no wave needs registers for both the K/V rows and the dK/dV
+// accumulators. Each staged Q/dO tile serves all 32 kP keys, so the more
+// keys a workgroup holds the fewer bytes it streams per product: six blocks
+// (168 registers per wave, three waves per SIMD) stream a third fewer than
+// four (256 registers, two waves per SIMD) and run the 128k workload's
+// backward about 2.5 % faster. The first four consumer waves also issue the
+// tile copies (a four-stage ring, one barrier per tile): a burst of copies
+// stalls the issuing wave at the address unit, and right after the barrier
+// the consumer has nothing urgent.
 #include <type_traits>
 
 #include "bwd_common.hpp"
@@ -26,12 +31,13 @@
 namespace uly {
 namespace {
 
-template <int D>
+template <int D, int kP>
 struct KvWs {
-  static constexpr int kWaves = 8;
+  static constexpr int kProducerWaves = kP;  // one per 32-key block; as many consumers
+  static constexpr int kWaves = 2 * kP;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kProducers = 256;  // waves 0-3
-  static constexpr int kKeys = 128;       // four blocks of 32
+  static constexpr int kProducers = 64 * kP;  // waves 0 .. kP-1
+  static constexpr int kKeys = 32 * kP;
   static constexpr int QT = 32;           // query rows per tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -41,24 +47,26 @@ struct KvWs {
   static constexpr int NSTAGE = 4;
   static constexpr int RING = NSTAGE * STAGE;
   static constexpr int PDS_BLOCK = 4 * 64 * 16;    // P and dS fragments of one key block
-  static constexpr int PDS = 2 * 4 * PDS_BLOCK;    // two tiles in flight, four key blocks
+  static constexpr int PDS = 2 * kP * PDS_BLOCK;   // two tiles in flight, kP key blocks
   static constexpr int LDS = RING + PDS;
-  static constexpr int kCopiers = kThreads - kProducers;  // the consumer waves
+  static constexpr int kCopiers = 256;              // the first four consumer waves
   static constexpr int LOADS = 2 * tile_loads<D, kCopiers, QT>() + 2;  // per consumer lane per stage
 };
 
-template <int D, bool kF32Out>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+template <int D, int kP, bool kF32Out>
+__global__ __attribute__((amdgpu_flat_work_group_size(KvWs<D, kP>::kThreads, KvWs<D, kP>::kThreads),
+                          amdgpu_waves_per_eu(kP / 2, kP / 2)))
 void dkdv_bf16_kernel(BwdParams p) {
-  using C = KvWs<D>;
+  using C = KvWs<D, kP>;
+  static_assert(kP % 2 == 0 && kP >= 4, "consumers cover two key blocks each; four of them copy");
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
   lds_char* ring = (lds_char*)smem_raw;
   lds_char* pds = ring + C::RING;
 
   const int tid = threadIdx.x;
   const int w = uniform(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const int kb = w & 3;
-  const bool producer = w < 4;
+  const bool producer = w < kP;
+  const int kb = producer ? w : 0;
   const int kvh = blockIdx.y;
   const int split = int(blockIdx.x) % p.splits;
   // heaviest key blocks first: the first blocks of the sequence, or with a
@@ -76,7 +84,7 @@ void dkdv_bf16_kernel(BwdParams p) {
   const uint32_t q_row = uint32_t(p.hq) * D * 2;
   const BwdScales sc = bwd_scales(p.absmax, p.scale);
 
-  // Queries that can see any of the 128 keys: [first_query(kv0), end of
+  // Queries that can see any of the workgroup's keys: [first_query(kv0), end of
   // the last key's document). The (query tile, q head) iterations over them, tiles from the
   // last one down and heads innermost, are dealt round-robin to the p.splits
   // workgroups of the key block; this one runs its share as local
@@ -99,15 +107,14 @@ void dkdv_bf16_kernel(BwdParams p) {
   struct Cursor {
     int qi, hi;
   };
-  const int step_q = p.splits / p.G, step_h = p.splits % p.G;
-  const Cursor first{split / p.G, split % p.G};
+  // (wave-uniform values, kept in scalar registers)
+  const int step_q = uniform(p.splits / p.G), step_h = uniform(p.splits % p.G);
+  const Cursor first{uniform(split / p.G), uniform(split % p.G)};
   auto advance = [&](Cursor& c) {
-    c.qi += step_q;
-    c.hi += step_h;
-    if (c.hi >= p.G) {
-      c.hi -= p.G;
-      ++c.qi;
-    }
+    const int h = c.hi + step_h;
+    const bool wrap = h >= p.G;
+    c.hi = uniform(wrap ? h - p.G : h);
+    c.qi = uniform(c.qi + step_q + (wrap ? 1 : 0));
   };
   auto tile_q0 = [&](const Cursor& c) { return (qt0 + n_qt - 1 - c.qi) * C::QT; };
   auto tile_head = [&](const Cursor& c) { return kvh * p.G + c.hi; };
@@ -121,7 +128,7 @@ void dkdv_bf16_kernel(BwdParams p) {
   auto sees = [&](const Cursor& c) { return sees_block(c, kw0, kbd.w_lo_first, w_de_last); };
   // P (slots 0, 1) and dS (slots 2, 3) fragments of tile it for key block b
   auto pds_at = [&](int it, int b, int slot) {
-    return pds + (((it & 1) * 4 + b) * 4 + slot) * 1024 + lane * 16;
+    return pds + (((it & 1) * kP + b) * 4 + slot) * 1024 + lane * 16;
   };
   typedef __attribute__((address_space(3))) bf16x8_t lds_frag;
 
@@ -149,11 +156,12 @@ void dkdv_bf16_kernel(BwdParams p) {
         typedef __attribute__((address_space(3))) const float lds_float;
         lds_float* fl = (lds_float*)(qt + 2 * C::TQ);
         const bool need_mask = (qs < kbd.w_lo_last) || (qs + C::QT > w_de_first);
-        // All operand reads of the tile go out before the first MFMA, so the
-        // 2 KS products run back to back instead of each waiting on its read.
+        // Operand reads run kAhead product steps ahead of the products
+        // (all of them at once when the registers allow).
+        constexpr int kAhead = kP > 4 ? 2 : C::KS;
         bf16x8_t qa[C::KS], da[C::KS];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+        for (int ks = 0; ks < kAhead; ++ks) {
           qa[ks] = frag_rows_at<D>(qt, ro.off[ks]);
           da[ks] = frag_rows_at<D>(dt, ro.off[ks]);
         }
@@ -165,10 +173,14 @@ void dkdv_bf16_kernel(BwdParams p) {
           l4[r4] = *(lds_f32x4*)(fl + 8 * r4 + 4 * half);
           d4[r4] = *(lds_f32x4*)(fl + 64 + 8 * r4 + 4 * half);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kAhead == C::KS) __builtin_amdgcn_sched_barrier(0);
         f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
+          if (ks + kAhead < C::KS) {
+            qa[ks + kAhead] = frag_rows_at<D>(qt, ro.off[ks + kAhead]);
+            da[ks + kAhead] = frag_rows_at<D>(dt, ro.off[ks + kAhead]);
+          }
           s = mfma_f16(qa[ks], kf[ks], s);
           dp = mfma_f16(da[ks], vf[ks], dp);
         }
@@ -210,7 +222,7 @@ void dkdv_bf16_kernel(BwdParams p) {
 
   // consumer: dV^T += dO^T P (dk_role false) or dK^T += Q^T dS (true) over
   // the 32 queries of each tile, for key blocks cb and cb + 1
-  const int cw = w - 4;
+  const int cw = w - kP;
   const bool dk_role = cw & 1;
   const int cb = 2 * (cw >> 1);
   int cb_k0[2], cb_lo[2], cb_de[2];
@@ -228,25 +240,38 @@ void dkdv_bf16_kernel(BwdParams p) {
   TrFragOffsets<D> to;  // transposed reads over 16-row steps
   to.init(lane);
   const int ctid = tid - C::kProducers;
-  auto issue = [&](int it, const Cursor& c) {
-    lds_char* st = stage(it);
-    const int head = tile_head(c);
-    const int qs = tile_q0(c);
-    const int rows = min(C::QT, p.N - qs);
-    const int64_t off = (int64_t(qs) * p.hq + head) * D * 2;
-    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.q16 + off, uint32_t(rows) * q_row), q_row, st, ctid);
-    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(p.do16 + off, uint32_t(rows) * q_row), q_row,
-                                            st + C::TQ, ctid);
-    // lse2 and delta of the tile's rows (every consumer wave copies the same values)
-    const int64_t foff = int64_t(head) * p.N + qs;
-    dma_to_lds<4>(make_rsrc_uniform(p.lse2 + foff, uint32_t(rows) * 4), st + 2 * C::TQ, lane * 4);
-    dma_to_lds<4>(make_rsrc_uniform(p.delta + foff, uint32_t(rows) * 4), st + 2 * C::TQ + 256, lane * 4);
-  };
+  const bool copier = ctid < C::kCopiers;
+  // The copies' source offsets follow the copy cursor by additions too:
+  // elements (qs * hq + head) * D of Q / dO and head * N + qs of lse2 / delta,
+  // in scalar registers.
+  const int64_t e_q = int64_t(uniform(p.hq)) * D, e_n = uniform(p.N);
+  const int64_t e_step = -int64_t(C::QT) * step_q * e_q + step_h * D, e_wrap = -int64_t(C::QT) * e_q - int64_t(p.G) * D;
+  const int64_t f_step = -int64_t(C::QT) * step_q + step_h * e_n, f_wrap = -int64_t(C::QT) - int64_t(p.G) * e_n;
   Cursor c_issue = first;  // at the tile to copy next
-  if (it0 < it1) issue(it0, c_issue);
-  advance(c_issue);
-  if (it0 + 1 < it1) issue(it0 + 1, c_issue);
-  advance(c_issue);
+  int64_t e_off = int64_t(tile_q0(first)) * e_q + int64_t(tile_head(first)) * D;
+  int64_t f_off = int64_t(tile_head(first)) * e_n + tile_q0(first);
+  auto advance_issue = [&]() {
+    const bool wrap = c_issue.hi + step_h >= p.G;
+    advance(c_issue);
+    e_off += e_step + (wrap ? e_wrap : 0);
+    f_off += f_step + (wrap ? f_wrap : 0);
+  };
+  auto issue = [&](int it) {
+    lds_char* st = stage(it);
+    const int qs = uniform(tile_q0(c_issue));
+    const uint32_t rows = uint32_t(min(C::QT, p.N - qs));
+    const char* qsrc = p.q16 + e_off * 2;
+    const char* dsrc = p.do16 + e_off * 2;
+    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(qsrc, rows * q_row), q_row, st, ctid);
+    issue_tile<D, C::kCopiers, C::QT, true>(make_rsrc_uniform(dsrc, rows * q_row), q_row, st + C::TQ, ctid);
+    // lse2 and delta of the tile's rows (every copying wave copies the same values)
+    dma_to_lds<4>(make_rsrc_uniform(p.lse2 + f_off, rows * 4), st + 2 * C::TQ, lane * 4);
+    dma_to_lds<4>(make_rsrc_uniform(p.delta + f_off, rows * 4), st + 2 * C::TQ + 256, lane * 4);
+  };
+  if (copier && it0 < it1) issue(it0);
+  advance_issue();
+  if (copier && it0 + 1 < it1) issue(it0 + 1);
+  advance_issue();
   Cursor c_jt = first;  // at the tile the consumers process next
   const int slot0 = dk_role ? 2 : 0;          // dS or P fragments
   const int src_off = dk_role ? 0 : C::TQ;    // Q or dO tile
@@ -255,8 +280,8 @@ void dkdv_bf16_kernel(BwdParams p) {
     if (it + 1 < it1) wait_vmcnt<C::LOADS>(); else wait_vmcnt<0>();
     __syncthreads();
     // the stage of tile it-2 is free: its consumer pass ended last iteration
-    if (it + 2 < it1) issue(it + 2, c_issue);
-    advance(c_issue);
+    if (copier && it + 2 < it1) issue(it + 2);
+    advance_issue();
     const int jt = it - 1;  // the tile the producers finished last iteration
     const bool run = jt >= it0 && (sees_block(c_jt, cb_k0[0], cb_lo[0], cb_de[0]) ||
                                    sees_block(c_jt, cb_k0[1], cb_lo[1], cb_de[1]));
@@ -316,15 +341,21 @@ void dkdv_bf16_kernel(BwdParams p) {
 
 }  // namespace
 
+// Producer waves (32 keys each) of the dK/dV kernel: six, so twelve waves,
+// three per SIMD, and 192 keys per workgroup.
+constexpr int kDkdvProducers = 6;
+
 template <int D, bool kF32Out>
-hipError_t launch_dkdv_bf16(const BwdParams& p, dim3 grid, hipStream_t stream) {
-  dkdv_bf16_kernel<D, kF32Out><<<grid, KvWs<D>::kThreads, 0, stream>>>(p);
+hipError_t launch_dkdv_bf16(BwdParams& p, int splits, int hk, hipStream_t stream) {
+  using C = KvWs<D, kDkdvProducers>;
+  p.n_tiles = (p.N + C::kKeys - 1) / C::kKeys;
+  dkdv_bf16_kernel<D, kDkdvProducers, kF32Out><<<dim3(p.n_tiles * splits, hk), C::kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template hipError_t launch_dkdv_bf16<128, false>(const BwdParams&, dim3, hipStream_t);
-template hipError_t launch_dkdv_bf16<128, true>(const BwdParams&, dim3, hipStream_t);
-template hipError_t launch_dkdv_bf16<64, false>(const BwdParams&, dim3, hipStream_t);
-template hipError_t launch_dkdv_bf16<64, true>(const BwdParams&, dim3, hipStream_t);
+template hipError_t launch_dkdv_bf16<128, false>(BwdParams&, int, int, hipStream_t);
+template hipError_t launch_dkdv_bf16<128, true>(BwdParams&, int, int, hipStream_t);
+template hipError_t launch_dkdv_bf16<64, false>(BwdParams&, int, int, hipStream_t);
+template hipError_t launch_dkdv_bf16<64, true>(BwdParams&, int, int, hipStream_t);
 
 }  // namespace uly

@@ -176,7 +176,9 @@ __device__ __forceinline__ void store4(char* dst, const float (&x)[4], bool add 
 
 // bf16 dK/dV kernel (its own translation unit, compiled with its own
 // scheduling flags); launches on `stream` and returns the launch status.
+// Sets p.n_tiles to the kernel's key blocks and launches splits of each for
+// the hk kv heads.
 template <int D, bool kF32Out>
-hipError_t launch_dkdv_bf16(const BwdParams& p, dim3 grid, hipStream_t stream);
+hipError_t launch_dkdv_bf16(BwdParams& p, int splits, int hk, hipStream_t stream);
 
 }  // namespace uly
