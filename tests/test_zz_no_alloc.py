@@ -62,7 +62,7 @@ def test_noalloc_matches_attn_bwd_on_consecutive_calls():
             uly.attn_bwd_noalloc(*t, *g, cfg.scale, run.cu_dev)
         torch.cuda.synchronize()
         free1 = torch.cuda.mem_get_info()[0]
-        if rep == 1:  # after the first round (module load), no device memory taken
+        if rep == 1:  # after the first repetition (module load), no device memory taken
             assert free1 >= free0, f"attn_bwd_noalloc took {free0 - free1} bytes of device memory"
         for (cfg, run, t), got, ref in zip(prepared, outs, refs):
             bits = (lambda x: x.view(torch.int16)) if got[0].dtype == torch.bfloat16 else (lambda x: x)
