@@ -50,7 +50,7 @@ struct KvWs {
   static constexpr int PDS = 2 * kP * PDS_BLOCK;   // two tiles in flight, kP key blocks
   static constexpr int LDS = RING + PDS;
   static constexpr int kCopiers = 256;              // the first four consumer waves
-  static constexpr int LOADS = 2 * tile_loads<D, kCopiers, QT>() + 2;  // per consumer lane per stage
+  static constexpr int LOADS = 2 * tile_loads<D, kCopiers, QT>() + 2;  // per copying lane per stage
 };
 
 template <int D, int kP, bool kF32Out>
