@@ -278,10 +278,13 @@ uly_status attn_merge(const void* const* o_parts, const float* const* lse_parts,
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd (and
- * attn_bwd_accumulate) needs for these sizes: the per-row delta_i =
- * dO_i . O_i and lse_i * log2(e) (float32 [hq][N] each) and the float32
- * partial dK/dV sums of the workgroups that share a key block (2 x 4 x
- * N x hk x D floats).
+ * attn_bwd_ex, attn_bwd_accumulate) needs for these sizes: the per-row
+ * delta_i = dO_i . O_i and lse_i * log2(e) (float32 [hq][N] each); for
+ * bf16 inputs also six float32 maxima and the power-of-two-scaled fp16
+ * copies of q, dout, k and v that the products read (2 x N x (hq + hk) x D
+ * halves); and the float32 partial dK/dV sums of the workgroups that share
+ * a key block (2 x 4 x N x hk x D floats). Each part starts on a 256-byte
+ * boundary.
  */
 uly_status attn_bwd_workspace_size(int64_t N, int hq, int hk, int D, uly_dtype dt,
                                    size_t* bytes);
