@@ -157,6 +157,23 @@ def test_bwd_c2_full():
     check_grads(cfg, got, oracle_attention(run))
 
 
+@pytest.mark.parametrize("lens", [None, [5000, 0, 1, 13000, 14767]])
+def test_bwd_d64_32k_full(lens):
+    """Head dim 64 at 32k tokens (the Llama-3.1-8B head group's shape with
+    D = 64: 171 key blocks of the dK/dV kernel, 128-row forward/dQ tiles),
+    one document and packed documents: every element of O, LSE, dQ, dK and
+    dV against the oracle."""
+    cfg = syn.custom(32768, 8, 32, 8, 64, "bf16", group=3, seed=64032)
+    run = Run(cfg, cu=None if lens is None else syn.cu_from_lengths(lens))
+    got = run_fwd_bwd(run)
+    ref = oracle_attention(run)
+    got_o = decode(dev_to_bits(got["o"]))
+    err_report("O", got_o, ref["o"])
+    assert_close(got_o, ref["o"], bf16_tol(ref["o"]), "O")
+    assert_close(got["lse"].cpu().numpy().astype(np.float64), ref["lse"], 1e-3, "LSE")
+    check_grads(cfg, got, ref)
+
+
 def _sum_rules(dk, dv, do):
     """Document sum rules over every key column of one document: sum_j dK_j = 0
     (softmax is invariant to shifting every score of a row) and sum_j dV_j =
